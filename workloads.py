@@ -1,0 +1,361 @@
+"""Seeded synthetic inputs for paged, variable-length attention.
+
+This module only *draws* inputs: sequence lengths, query/key/value values and
+block tables.  It holds none of the attention arithmetic, so both the CPU oracle
+(``oracle/``) and the GPU library (``paged_varlen_flashattention_amd``) can be
+fed from it without sharing any of the method's code.
+
+Workloads follow the shapes of the pages:
+
+* page "vLLM Triton unified attention notes", section ``test_triton_unified_attn``:
+  packed queries ``[sum(q_len), Hq, D]``, a paged cache
+  ``[num_blocks, block_size, Hkv, D]``, ``cu_seqlens_q`` as an inclusive prefix
+  sum with a leading 0, and one block table row per sequence whose ids are drawn
+  at random from the block pool;
+* page "Fused Attention" (FA2 tutorial listing, benchmark section): dense
+  batch 4 x 32 heads, N(0,1) values, which we express as one contiguous block
+  table per sequence.
+
+Every random draw comes from ``numpy.random.default_rng`` seeded by
+``SeedSequence([config_id, stream_id, chunk])``; streams are 0 lengths, 1 q,
+2 k, 3 v, 4 block ids.  Large tensors are drawn in fixed chunks of
+``CHUNK`` elements (each chunk its own seed), so the values do not depend on how
+many threads draw them.
+"""
+from __future__ import annotations
+
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+CHUNK = 1 << 22          # elements per independently seeded chunk
+FP8_MAX = 448.0          # largest finite OCP E4M3FN magnitude
+
+STREAM_LENGTHS, STREAM_Q, STREAM_K, STREAM_V, STREAM_BLOCKS = 0, 1, 2, 3, 4
+
+TORCH_DTYPES = {
+    "bf16": torch.bfloat16,
+    "fp16": torch.float16,
+    "fp8_e4m3fn": torch.float8_e4m3fn,
+}
+
+
+@dataclass
+class Workload:
+    """One batch of inputs for a paged varlen attention call (CPU tensors)."""
+    name: str
+    q: torch.Tensor                 # [T, Hq, D] bf16 / fp16
+    k_cache: torch.Tensor           # [NB, bs, Hkv, D] bf16 / fp16 / fp8_e4m3fn
+    v_cache: torch.Tensor           # [NB, bs, Hkv, D]
+    cu_seqlens_q: torch.Tensor      # [S+1] int32, cu[0] = 0
+    seqused_k: torch.Tensor         # [S] int32, kv length including the new queries
+    block_table: torch.Tensor       # [S, W] int32
+    softmax_scale: float
+    causal: bool
+    k_scale: Optional[float] = None  # fp32 per-tensor dequant scales (fp8 KV only)
+    v_scale: Optional[float] = None
+    num_splits: int = 1
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def q_lens(self) -> np.ndarray:
+        cu = self.cu_seqlens_q.numpy().astype(np.int64)
+        return cu[1:] - cu[:-1]
+
+    @property
+    def kv_lens(self) -> np.ndarray:
+        return self.seqused_k.numpy().astype(np.int64)
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.seqused_k.numel())
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def num_q_heads(self) -> int:
+        return int(self.q.shape[1])
+
+    @property
+    def num_kv_heads(self) -> int:
+        return int(self.k_cache.shape[2])
+
+    @property
+    def head_size(self) -> int:
+        return int(self.q.shape[2])
+
+    @property
+    def block_size(self) -> int:
+        return int(self.k_cache.shape[1])
+
+    @property
+    def num_blocks(self) -> int:
+        return int(self.k_cache.shape[0])
+
+    @property
+    def max_seqlen_q(self) -> int:
+        return int(self.q_lens.max()) if self.num_seqs else 0
+
+    @property
+    def max_seqlen_k(self) -> int:
+        return int(self.kv_lens.max()) if self.num_seqs else 0
+
+    def visible_pairs(self) -> int:
+        """Number of visible (query, key) pairs per query head (causal: bottom-right aligned)."""
+        total = 0
+        for ql, kl in zip(self.q_lens.tolist(), self.kv_lens.tolist()):
+            if self.causal:
+                ctx = kl - ql
+                # query i sees keys 0 .. ctx + i
+                total += ql * ctx + ql * (ql + 1) // 2
+            else:
+                total += ql * kl
+        return total
+
+    def flops(self) -> float:
+        """Algorithmic FLOPs: two matmuls of 2*D flops per visible pair and head."""
+        return 4.0 * self.head_size * self.num_q_heads * self.visible_pairs()
+
+    def kv_bytes(self) -> int:
+        """K and V bytes read once per (sequence, kv head)."""
+        elt = self.k_cache.element_size()
+        return int(self.kv_lens.sum()) * self.num_kv_heads * self.head_size * elt * 2
+
+
+# --------------------------------------------------------------------------- draws
+
+def _seed(config_id: int, stream: int, chunk: int = 0) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence([int(config_id), int(stream), int(chunk)]))
+
+
+def _threads() -> int:
+    n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def normal_tensor(config_id: int, stream: int, shape: Sequence[int], dtype: str) -> torch.Tensor:
+    """N(0,1) values rounded (round-to-nearest-even, by torch's cast) to bf16 or fp16."""
+    n = int(np.prod(shape))
+    out = torch.empty(n, dtype=TORCH_DTYPES[dtype])
+    step = 64 * CHUNK
+    for lo in range(0, n, step):
+        hi = min(n, lo + step)
+        # lo is a multiple of CHUNK, so chunk seeds do not depend on the step
+        vals = _normal_range(config_id, stream, lo, hi)
+        out[lo:hi] = torch.from_numpy(vals).to(out.dtype)
+    return out.view(*shape)
+
+
+def _normal_range(config_id: int, stream: int, lo: int, hi: int) -> np.ndarray:
+    """Elements [lo, hi) of the chunked stream (lo, hi multiples of CHUNK except at the end)."""
+    assert lo % CHUNK == 0
+    out = np.empty(hi - lo, dtype=np.float32)
+    c0 = lo // CHUNK
+    nchunks = (hi - lo + CHUNK - 1) // CHUNK
+
+    def fill(k: int) -> None:
+        a = k * CHUNK
+        b = min(hi - lo, a + CHUNK)
+        _seed(config_id, stream, c0 + k).standard_normal(b - a, dtype=np.float32, out=out[a:b])
+
+    if nchunks <= 1:
+        for k in range(nchunks):
+            fill(k)
+    else:
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(fill, range(nchunks)))
+    return out
+
+
+def fp8_quantised_tensor(config_id: int, stream: int, shape: Sequence[int]):
+    """N(0,1) values quantised to OCP E4M3FN with one per-tensor scale.
+
+    scale = amax(|x|) / 448 over the whole tensor; codes = RNE(x / scale), clamped
+    to +-448, by torch's float8_e4m3fn cast.  Returns (codes, scale) where the
+    dequantised value is codes * scale.
+    """
+    n = int(np.prod(shape))
+    vals = _normal_range(config_id, stream, 0, n)
+    amax = float(np.abs(vals).max()) if n else 1.0
+    scale = np.float32(amax / FP8_MAX)
+    codes = torch.empty(n, dtype=torch.float8_e4m3fn)
+    step = 64 * CHUNK
+    for lo in range(0, n, step):
+        hi = min(n, lo + step)
+        x = torch.from_numpy(vals[lo:hi]) / float(scale)
+        codes[lo:hi] = x.clamp_(-FP8_MAX, FP8_MAX).to(torch.float8_e4m3fn)
+    return codes.view(*shape), float(scale)
+
+
+def block_tables(config_id: int, num_seqs: int, width: int, num_blocks: int, mode: str,
+                 kv_lens: Optional[Sequence[int]] = None, block_size: int = 16,
+                 poison_unused: bool = False) -> torch.Tensor:
+    """Per-sequence page tables.
+
+    mode 'perm': a seeded random permutation of physical ids, perm(NB)[:S*W];
+    mode 'replace': ids drawn uniformly with replacement from [0, NB);
+    mode 'contiguous': sequence s owns blocks s*W .. s*W + W - 1.
+    With poison_unused, entries past ceil(kv_len / block_size) are set to -1.
+    """
+    rng = _seed(config_id, STREAM_BLOCKS)
+    if mode == "perm":
+        if num_seqs * width > num_blocks:
+            raise ValueError("pool too small for a permutation table")
+        ids = rng.permutation(num_blocks)[: num_seqs * width].reshape(num_seqs, width)
+    elif mode == "replace":
+        ids = rng.integers(0, num_blocks, size=(num_seqs, width))
+    elif mode == "contiguous":
+        ids = np.arange(num_seqs * width).reshape(num_seqs, width)
+        if num_seqs * width > num_blocks:
+            raise ValueError("pool too small for contiguous tables")
+    else:
+        raise ValueError(mode)
+    ids = ids.astype(np.int32)
+    if poison_unused:
+        assert kv_lens is not None
+        for s, kl in enumerate(kv_lens):
+            used = (int(kl) + block_size - 1) // block_size
+            ids[s, used:] = -1
+    return torch.from_numpy(np.ascontiguousarray(ids))
+
+
+def uniform_ints(config_id: int, lo: int, hi: int, n: int, stream: int = STREAM_LENGTHS,
+                 chunk: int = 0) -> np.ndarray:
+    """n integers uniform on [lo, hi] inclusive."""
+    return _seed(config_id, stream, chunk).integers(lo, hi + 1, size=n)
+
+
+# --------------------------------------------------------------------------- builders
+
+def make_paged(name: str, seed_id: int, q_lens: Sequence[int], kv_lens: Sequence[int],
+               num_q_heads: int, num_kv_heads: int, head_size: int = 128,
+               block_size: int = 16, num_blocks: Optional[int] = None,
+               width: Optional[int] = None, dtype: str = "bf16", kv_dtype: Optional[str] = None,
+               table_mode: str = "perm", causal: bool = True,
+               softmax_scale: Optional[float] = None, num_splits: int = 1,
+               poison_unused: bool = False) -> Workload:
+    """A paged varlen batch with N(0,1) q/k/v, seeded by ``seed_id``."""
+    q_lens = [int(x) for x in q_lens]
+    kv_lens = [int(x) for x in kv_lens]
+    if len(q_lens) != len(kv_lens):
+        raise ValueError("q_lens and kv_lens differ in length")
+    for ql, kl in zip(q_lens, kv_lens):
+        if ql > kl:
+            raise ValueError("q_len > kv_len is not a valid input")
+    kv_dtype = kv_dtype or dtype
+    S = len(q_lens)
+    T = sum(q_lens)
+    need = max([(kl + block_size - 1) // block_size for kl in kv_lens] + [1])
+    W = width or need
+    if W < need:
+        raise ValueError("block table too narrow")
+    if num_blocks is None:
+        num_blocks = S * W if table_mode in ("perm", "contiguous") else max(S * W, 1)
+    cu = np.zeros(S + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(q_lens)
+    q = normal_tensor(seed_id, STREAM_Q, (T, num_q_heads, head_size), dtype)
+    cache_shape = (num_blocks, block_size, num_kv_heads, head_size)
+    k_scale = v_scale = None
+    if kv_dtype == "fp8_e4m3fn":
+        k_cache, k_scale = fp8_quantised_tensor(seed_id, STREAM_K, cache_shape)
+        v_cache, v_scale = fp8_quantised_tensor(seed_id, STREAM_V, cache_shape)
+    else:
+        k_cache = normal_tensor(seed_id, STREAM_K, cache_shape, kv_dtype)
+        v_cache = normal_tensor(seed_id, STREAM_V, cache_shape, kv_dtype)
+    bt = block_tables(seed_id, S, W, num_blocks, table_mode, kv_lens, block_size, poison_unused)
+    return Workload(
+        name=name, q=q, k_cache=k_cache, v_cache=v_cache,
+        cu_seqlens_q=torch.from_numpy(cu), seqused_k=torch.tensor(kv_lens, dtype=torch.int32),
+        block_table=bt,
+        softmax_scale=softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(head_size),
+        causal=causal, k_scale=k_scale, v_scale=v_scale, num_splits=num_splits,
+        meta={"seed_id": seed_id, "table_mode": table_mode, "dtype": dtype, "kv_dtype": kv_dtype},
+    )
+
+
+def config1() -> Workload:
+    """Tiny paged varlen batch (page 1, test_triton_unified_attn shapes): 3 sequences,
+    q_lens [1,5,129], kv_lens [1328,18,463], 4/4 heads, D 128, bs 16, 512 blocks,
+    permutation block tables, bf16, causal, scale 1/sqrt(128)."""
+    return make_paged("c1_tiny_paged", 1, [1, 5, 129], [1328, 18, 463], 4, 4, 128,
+                      block_size=16, num_blocks=512, width=83, dtype="bf16",
+                      table_mode="perm", causal=True)
+
+
+def config2(causal: bool = True, batch: int = 4, heads: int = 32, seq: int = 4096) -> Workload:
+    """Dense FA2 forward (page 3 tutorial benchmark family) as a paged layout with
+    contiguous tables: batch 4, 32 heads, N 4096, D 128, fp16, causal or not."""
+    bs = 16
+    W = seq // bs
+    return make_paged(f"c2_dense_b{batch}_h{heads}_n{seq}_{'causal' if causal else 'full'}", 2,
+                      [seq] * batch, [seq] * batch, heads, heads, 128, block_size=bs,
+                      num_blocks=batch * W, width=W, dtype="fp16", table_mode="contiguous",
+                      causal=causal)
+
+
+def config3_lengths(n: int = 256) -> np.ndarray:
+    return uniform_ints(3, 512, 8192, n)
+
+
+def config3(num_splits: int = 1, num_seqs: int = 256, num_blocks: int = 65536) -> Workload:
+    """Decode-heavy paged GQA batch: 256 x (q 1, kv U{512..8192}), 32/8 heads, bs 16,
+    tables with replacement over a 65536-block pool, bf16."""
+    kv = config3_lengths(num_seqs)
+    return make_paged(f"c3_decode_s{num_seqs}_splits{num_splits}", 3, [1] * num_seqs, kv, 32, 8, 128,
+                      block_size=16, num_blocks=num_blocks, width=512, dtype="bf16",
+                      table_mode="replace", causal=True, num_splits=num_splits)
+
+
+def config4_lengths():
+    dec_kv = uniform_ints(4, 1024, 16384, 64)
+    prefix = uniform_ints(4, 0, 8192, 4, chunk=1)
+    q_lens = [1] * 64 + [2048] * 4
+    kv_lens = list(dec_kv) + [int(p) + 2048 for p in prefix]
+    return q_lens, kv_lens
+
+
+def config4() -> Workload:
+    """Mixed chunked prefill: 64 decode sequences (q 1, kv U{1024..16384}) + 4 prefill
+    chunks of 2048 tokens with cached prefix U{0..8192}; 64/8 heads, bs 32, bf16, causal."""
+    q_lens, kv_lens = config4_lengths()
+    return make_paged("c4_mixed_chunked_prefill", 4, q_lens, kv_lens, 64, 8, 128, block_size=32,
+                      num_blocks=34816, width=512, dtype="bf16", table_mode="perm", causal=True)
+
+
+def config5(num_splits: int = 32, kv_len: int = 131072) -> Workload:
+    """Long-context split-KV: q_lens [1,16], kv 131072, 64/8 heads, bs 16, fp8 e4m3fn KV
+    with per-tensor scales, bf16 q, 32 splits."""
+    W = kv_len // 16
+    return make_paged(f"c5_long_fp8_splits{num_splits}", 5, [1, 16], [kv_len, kv_len], 64, 8, 128,
+                      block_size=16, num_blocks=2 * W, width=W, dtype="bf16",
+                      kv_dtype="fp8_e4m3fn", table_mode="perm", causal=True,
+                      num_splits=num_splits)
+
+
+CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
+
+
+def random_small(seed: int, *, max_seqs: int = 4, max_kv: int = 70, heads=(4, 2),
+                 block_size: Optional[int] = None, head_size: int = 128, dtype: str = "bf16",
+                 kv_dtype: Optional[str] = None, causal: Optional[bool] = None,
+                 allow_empty_q: bool = True) -> Workload:
+    """A tiny random paged batch for brute-force comparisons (seed ids 1000 + seed)."""
+    rng = _seed(1000 + seed, STREAM_LENGTHS)
+    S = int(rng.integers(1, max_seqs + 1))
+    kv = rng.integers(1, max_kv + 1, size=S)
+    lo = 0 if allow_empty_q else 1
+    ql = [int(rng.integers(lo, k + 1)) for k in kv]
+    bs = block_size or int(rng.choice([16, 32]))
+    c = bool(rng.integers(0, 2)) if causal is None else causal
+    hq, hkv = heads
+    return make_paged(f"rand{seed}", 1000 + seed, ql, kv.tolist(), hq, hkv, head_size,
+                      block_size=bs, num_blocks=None, dtype=dtype, kv_dtype=kv_dtype,
+                      table_mode="perm", causal=c,
+                      softmax_scale=float(rng.uniform(0.02, 0.2)))
