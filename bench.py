@@ -1,0 +1,251 @@
+"""Benchmark of the unified paged varlen attention forward on one MI355X.
+
+Default workload (the headline): dense FA2 forward, batch 4 x 32 heads x 4096
+tokens, head_dim 128, fp16, expressed as a paged cache with one contiguous block
+table per sequence (block_size 16).  One step = one causal call + one full
+(non-causal) call of ua_unified_attention on the same inputs.  The value is
+algorithmic attention TFLOP/s: 4 * D * (visible query-key pairs) * heads,
+summed over both calls, divided by the step time.
+
+Other workloads (``--config c3|c4|c5``) are measured the same way for the
+record; c3 and c5 report KV-read GB/s.
+
+Prints ONE JSON line.  Inputs are resident in HBM before the timed region;
+K steps run back to back between two device synchronisations.  Per-launch
+durations come from HIP events recorded on the stream the kernels run on.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_MFMA_TFLOPS = 2516.6      # MI355X dense bf16 / fp16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="c2", choices=["c2", "c3", "c4", "c5"])
+    ap.add_argument("--splits", type=int, default=None, help="override num_splits (c3/c5)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target wall time of the oracle CPU-baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "paged_varlen_flashattention_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel_tag: str):
+    """HBM bytes per launch measured by rocprofv3 counters (profiles/traffic_*.json),
+    only while the kernel sources are unchanged since they were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel_tag}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def build_calls(cfg: str, splits_override):
+    """Returns (workload description, list of (label, workload, num_splits))."""
+    import workloads as wk
+    if cfg == "c2":
+        wl_c = wk.config2(causal=True)
+        wl_f = wk.Workload(**{**wl_c.__dict__, "causal": False,
+                              "name": wl_c.name.replace("causal", "full")})
+        return ("dense_fa2_fwd_b4_h32_n4096_d128_fp16_causal_and_full",
+                [("full", wl_f, 1), ("causal", wl_c, 1)])
+    if cfg == "c3":
+        s = 8 if splits_override is None else splits_override
+        return (f"decode_paged_gqa_256seq_32q8kv_bs16_splits{s}", [("decode", wk.config3(), s)])
+    if cfg == "c4":
+        return ("mixed_chunked_prefill_64dec_4x2048_64q8kv_bs32", [("mixed", wk.config4(), 1)])
+    s = 32 if splits_override is None else splits_override
+    return (f"long_ctx_fp8kv_2x131072_64q8kv_splits{s}", [("long", wk.config5(), s)])
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build measures one GPU only: run bench.py with --gpus 1 "
+                          "(the attention call has no cross-GPU step; sharding is described in "
+                          "DESIGN.md)", "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_varlen_flashattention_amd as ua
+
+    if not torch.cuda.is_available():
+        raise RuntimeError("bench.py needs a GPU")
+    ua.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    workload_name, calls = build_calls(args.config, args.splits)
+    prepared = []
+    for label, wl, splits in calls:
+        d = {
+            "q": wl.q.to(dev), "k": wl.k_cache.to(dev), "v": wl.v_cache.to(dev),
+            "cu": wl.cu_seqlens_q.to(dev), "kv": wl.seqused_k.to(dev), "bt": wl.block_table.to(dev),
+            "ks": None if wl.k_scale is None else torch.tensor([wl.k_scale], device=dev),
+            "vs": None if wl.v_scale is None else torch.tensor([wl.v_scale], device=dev),
+        }
+        d["out"] = torch.empty_like(d["q"])
+        ws = None
+        if splits > 1:
+            ws = torch.empty(ua.workspace_size(wl.num_tokens, wl.num_q_heads, 128, splits),
+                             dtype=torch.uint8, device=dev)
+        prepared.append((label, wl, splits, d, ws))
+    stream = torch.cuda.current_stream()
+
+    def call(wl, splits, d, ws):
+        ua.unified_attention(d["q"], d["k"], d["v"], d["out"], d["cu"], d["kv"], d["bt"],
+                             wl.max_seqlen_q, wl.max_seqlen_k, wl.softmax_scale, wl.causal,
+                             d["ks"], d["vs"], num_splits=splits, workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        for _, wl, splits, d, ws in prepared:
+            call(wl, splits, d, ws)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = {label: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(K)] for label, *_ in prepared}
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for k in range(K):
+        for label, wl, splits, d, ws in prepared:
+            e0, e1 = ev[label][k]
+            e0.record(stream)
+            call(wl, splits, d, ws)
+            e1.record(stream)
+    t_stop.record(stream)
+    torch.cuda.synchronize()
+    ms_total = t_start.elapsed_time(t_stop)
+    ms_per_step = ms_total / K
+
+    per = {}
+    for label, wl, splits, d, ws in prepared:
+        durs = np.array([a.elapsed_time(b) for a, b in ev[label]])
+        per[label] = {"ms_mean": float(durs.mean()), "ms_min": float(durs.min()),
+                      "ms_median": float(np.median(durs)), "flops": wl.flops(),
+                      "kv_bytes": wl.kv_bytes(), "splits": splits}
+
+    compute_bound = args.config in ("c2", "c4")
+    if compute_bound:
+        total_flops = sum(p["flops"] for p in per.values())
+        value = total_flops / (ms_per_step * 1e-3) / 1e12
+        metric, unit = "attention TFLOP/s (prefill)", "TFLOP/s"
+    else:
+        total_bytes = sum(p["kv_bytes"] for p in per.values())
+        value = total_bytes / (ms_per_step * 1e-3) / 1e9
+        metric, unit = "KV-read GB/s (decode)", "GB/s"
+
+    def roofline(label, tag):
+        p = per[label]
+        if compute_bound:
+            ach = p["flops"] / (p["ms_mean"] * 1e-3) / 1e12
+            r = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
+                 "frac": round(ach / PEAK_MFMA_TFLOPS, 4)}
+        else:
+            ach = p["kv_bytes"] / (p["ms_mean"] * 1e-3) / 1e9
+            r = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                 "frac": round(ach / PEAK_HBM_GBS, 4)}
+        r["traffic"] = traffic_from_profiles(tag)
+        r["launch_ms_mean"] = round(p["ms_mean"], 4)
+        return r
+
+    dominant = max(per, key=lambda k: per[k]["ms_mean"])
+    result = {
+        "metric": metric, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp16" if args.config == "c2" else "bf16",
+        "data": "synthetic (seeded N(0,1) q/k/v, paged cache)",
+        "config": {"workload": workload_name, "calls_per_step": [p[0] for p in prepared]},
+        "roofline": roofline(dominant, f"{args.config}_{dominant}"),
+        "per_call": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                     for k, v in per.items()},
+    }
+    for label in per:
+        if label != dominant:
+            result[f"roofline_{label}"] = roofline(label, f"{args.config}_{label}")
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(prepared, compute_bound, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(prepared, compute_bound: bool, target_s: float) -> dict:
+    """The fp64 C oracle, as it stands, on a bounded sample of the same rows,
+    timed on the host cores; scaled to the metric's unit."""
+    import numpy as np
+
+    import oracle
+
+    threads = os.cpu_count() or 1
+    rng = np.random.default_rng(0)
+    work = 0.0
+    elapsed = 0.0
+    nrows = 0
+    n = max(16, threads * 4)
+    while elapsed < target_s and n <= 1 << 22:
+        for label, wl, splits, d, ws in prepared:
+            toks = rng.integers(0, wl.num_tokens, size=n)
+            heads = rng.integers(0, wl.num_q_heads, size=n)
+            rows = np.stack([toks, heads], axis=1)
+            t0 = time.perf_counter()
+            oracle.attention_workload(wl, rows=rows, threads=threads)
+            elapsed += time.perf_counter() - t0
+            nrows += n
+            work += row_work(wl, toks, compute_bound)
+        n *= 2
+    value = work / elapsed / (1e12 if compute_bound else 1e9)
+    return {"value": round(value, 6), "unit": "TFLOP/s" if compute_bound else "GB/s",
+            "cores": threads, "kind": "oracle",
+            "sample": f"{nrows} random (token, head) rows of the same workload, fp64 C oracle "
+                      f"(OpenMP, {threads} threads), {elapsed:.1f} s on {platform.processor() or 'host'}"}
+
+
+def row_work(wl, toks, compute_bound: bool) -> float:
+    """Algorithmic flops (or KV bytes) of the given rows."""
+    import numpy as np
+    cu = wl.cu_seqlens_q.numpy()
+    kv = wl.kv_lens
+    s = np.searchsorted(cu, toks, side="right") - 1
+    ql = cu[s + 1] - cu[s]
+    i = toks - cu[s]
+    vis = np.minimum(kv[s], kv[s] - ql + i + 1) if wl.causal else kv[s]
+    if compute_bound:
+        return float(4.0 * wl.head_size * vis.sum())
+    G = wl.num_q_heads // wl.num_kv_heads
+    return float((vis * wl.head_size * wl.k_cache.element_size() * 2 / G).sum())
+
+
+if __name__ == "__main__":
+    main()

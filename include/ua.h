@@ -1,0 +1,208 @@
+/*
+ * ua.h -- C ABI of the unified paged, variable-length attention forward for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * One call computes, for a batch of sequences whose query tokens are packed
+ * back to back, softmax(q K^T * scale) V against a paged KV cache, per query
+ * head, with grouped-query heads, a causal or full mask, and an optional split
+ * of the key range into partial results merged by a log-sum-exp combine.
+ *
+ * Where each operation is defined (citations are to the pages this library
+ * implements):
+ *   - the attention itself: page "flashatten takeaways EP2 工程", section
+ *     "kv cache", the boxed formula O = softmax(q K^T / sqrt(d)) V over every
+ *     cached token;
+ *   - packed queries, cu_seqlens_q, the paged cache layout [num_blocks,
+ *     block_size, kv_heads, head_size] with its four strides, per-sequence
+ *     block tables, num_queries_per_kv = Hq / Hkv, context_len and the fp8
+ *     dequantisation scales: page "vLLM Triton unified attention notes",
+ *     sections test_triton_unified_attn, unified_attention and
+ *     kernel_unified_attention_2d;
+ *   - the split-KV partial pass and the combine that corrects the partials:
+ *     page "flashatten takeaways EP2 工程", section "源代码接口" (the
+ *     run_flash_splitkv_fwd interface and its combine launch, at most 128
+ *     splits); page "Fused Attention", section FlashDecoding;
+ *   - the log-sum-exp of each output row: page "Fused Attention", the
+ *     tutorial's forward epilogue (m += log2 l, stored per row).
+ *
+ * Conventions shared by every entry point:
+ *   - All data pointers are DEVICE pointers owned by the caller.  The library
+ *     allocates no memory, keeps no mutable global state and is thread-safe.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on it: no host synchronisation, no device-to-host copy.
+ *   - Element strides are in elements, not bytes; the innermost (head_size)
+ *     stride is always 1.
+ *   - Host-checkable violations return a negative ua_status and enqueue
+ *     nothing.  Data-dependent violations (q_len > kv_len, a block id outside
+ *     [0, num_blocks), max_seqlen_* smaller than the true maximum, a
+ *     cu_seqlens_q that is not non-decreasing) are undefined behaviour and are
+ *     not checked on the device.
+ */
+#ifndef UA_H
+#define UA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define UA_ABI_VERSION 1u
+
+typedef enum {
+    UA_OK = 0,
+    UA_ERR_INVALID_ARG = -1,   /* null pointer, bad size, stride or alignment, abi mismatch */
+    UA_ERR_UNSUPPORTED = -2,   /* valid but not implemented: head_size != 128, fp8 q, ... */
+    UA_ERR_WORKSPACE = -3,     /* num_splits > 1 without a large enough workspace */
+    UA_ERR_HIP = -4            /* the HIP runtime refused a launch */
+} ua_status;
+
+typedef enum {
+    UA_BF16 = 0,               /* bfloat16 */
+    UA_FP16 = 1,               /* IEEE binary16 */
+    UA_FP8_E4M3FN = 2          /* OCP 8-bit E4M3FN (bias 7, max 448, no inf); KV cache only */
+} ua_dtype;
+
+/*
+ * Arguments of one attention call.  Shapes use
+ *   S = num_seqs, T = num_tokens, Hq = num_q_heads, Hkv = num_kv_heads,
+ *   D = head_size, NB = num_blocks, bs = block_size, W = block_table_stride.
+ *
+ * q            [T, Hq, D] of q_dtype (bf16 or fp16); token t of sequence s is
+ *              row cu_seqlens_q[s] + i, i < q_len(s).  Strides q_stride_token,
+ *              q_stride_head.
+ * k_cache,     [NB, bs, Hkv, D] of kv_dtype (q_dtype, or fp8 e4m3fn).  Both
+ * v_cache      caches use the strides kv_stride_block, kv_stride_slot,
+ *              kv_stride_head.  Key position j of sequence s lives in physical
+ *              block block_table[s * W + j / bs], slot j % bs.
+ * out          [T, Hq, D] of q_dtype; strides o_stride_token, o_stride_head.
+ *              Rows of tokens that belong to no sequence are not written.
+ * cu_seqlens_q [S + 1] int32, cu_seqlens_q[0] = 0, non-decreasing; q_len(s) =
+ *              cu[s + 1] - cu[s] (0 allowed); cu[S] = T.
+ * seqused_k    [S] int32: kv_len(s), the number of keys of sequence s, which
+ *              includes its q_len(s) new tokens (kv_len >= q_len).
+ * block_table  [S, W] int32 physical block ids; entries at or past
+ *              ceil(kv_len(s) / bs) are never read (they may hold anything).
+ * max_seqlen_q, max_seqlen_k  caller-guaranteed upper bounds of q_len and
+ *              kv_len (they size the launch on the host).
+ * softmax_scale  finite and > 0 (scores are scale * q . k).
+ * causal       0: every query sees keys [0, kv_len).  1: query i of sequence
+ *              s sits at position kv_len - q_len + i and sees keys
+ *              [0, kv_len - q_len + i] (queries are the newest tokens).
+ * k_scale,     device fp32 scalars, required iff kv_dtype is fp8 (else NULL):
+ * v_scale      a stored code c means the value c * scale.
+ * num_splits   0 = choose automatically, 1 = no split, 2..128 = split each
+ *              query block's key range into that many contiguous chunks whose
+ *              partials (fp32 output + log-sum-exp) are merged by the combine
+ *              kernel on the same stream.
+ * workspace,   device scratch for the partials, at least
+ * workspace_bytes  ua_workspace_size(T, Hq, D, splits) bytes, 256-byte
+ *              aligned; may be NULL when no split is used.  Automatic split
+ *              choice (num_splits = 0) never picks a split the workspace
+ *              cannot hold.
+ * lse_out      optional [T, Hq] fp32 natural-log log-sum-exp of each row's
+ *              scaled scores (NULL = not written).
+ *
+ * Requirements checked on the host: abi_version == UA_ABI_VERSION; non-NULL
+ * q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table (when S > 0
+ * and T > 0); D == 128; Hq % Hkv == 0 and Hq / Hkv <= 128; bs a power of two
+ * in [16, 4096]; W >= ceil(max_seqlen_k / bs); all strides multiples of 8 and
+ * positive; q, out, k_cache, v_cache 16-byte aligned; num_splits <= 128.
+ * S == 0 or T == 0 is a no-op that returns UA_OK.
+ */
+typedef struct ua_attn_params {
+    uint32_t abi_version;
+    int32_t q_dtype;                 /* ua_dtype of q and out */
+    int32_t kv_dtype;                /* ua_dtype of k_cache and v_cache */
+    int32_t causal;
+
+    const void *q;
+    const void *k_cache;
+    const void *v_cache;
+    void *out;
+    const int32_t *cu_seqlens_q;
+    const int32_t *seqused_k;
+    const int32_t *block_table;
+    const float *k_scale;
+    const float *v_scale;
+    float *lse_out;
+    void *workspace;
+    uint64_t workspace_bytes;
+
+    int64_t q_stride_token, q_stride_head;
+    int64_t o_stride_token, o_stride_head;
+    int64_t kv_stride_block, kv_stride_slot, kv_stride_head;
+
+    int32_t num_seqs, num_tokens, num_q_heads, num_kv_heads;
+    int32_t head_size, block_size, num_blocks, block_table_stride;
+    int32_t max_seqlen_q, max_seqlen_k;
+    int32_t num_splits;
+    float softmax_scale;
+} ua_attn_params;
+
+/* The launch the library chose for a call (filled by ua_plan). */
+typedef struct ua_plan_info {
+    int32_t block_m;       /* query rows (token x head pairs) per workgroup */
+    int32_t block_q;       /* query tokens per workgroup = block_m / (Hq / Hkv) */
+    int32_t tile_n;        /* keys per KV tile */
+    int32_t num_waves;     /* 64-lane wavefronts per workgroup */
+    int32_t num_splits;    /* splits actually used (1 = no combine launch) */
+    int32_t reserved;
+    int64_t grid_x;        /* workgroups along (query block slot x kv head) */
+    int64_t grid_y;        /* workgroups along splits */
+} ua_plan_info;
+
+/*
+ * Attention forward (the unified paged varlen path).  Enqueues the attention
+ * kernel and, when more than one split is used, the combine kernel, on
+ * `stream`.  Returns UA_OK once enqueued; see ua_status for errors.
+ */
+ua_status ua_unified_attention(const ua_attn_params *p, void *stream);
+
+/*
+ * Log-sum-exp merge of split partials (page "flashatten takeaways EP2 工程",
+ * section "源代码接口"): for each row r (token, q head),
+ *   L = max_p lse[p, r];  w_p = exp(lse[p, r] - L);
+ *   out[r] = sum_p w_p * o[p, r] / sum_p w_p;  lse_out[r] = L + ln sum_p w_p.
+ * Splits with lse = -inf weigh 0; a row whose splits are all -inf gets out = 0
+ * and lse_out = -inf.
+ * o_partial    [num_splits, T, Hq, D] fp32, contiguous (normalised partials).
+ * lse_partial  [num_splits, T, Hq] fp32, contiguous, natural log.
+ * out          [T, Hq, D] of out_dtype (bf16 or fp16), strides o_stride_*.
+ * lse_out      optional [T, Hq] fp32 (NULL = not written).
+ * Requirements: 1 <= num_splits <= 128, D == 128, non-NULL o_partial,
+ * lse_partial, out; 16-byte aligned pointers; strides multiples of 8.
+ */
+ua_status ua_split_kv_combine(const float *o_partial, const float *lse_partial,
+                              int32_t num_splits, int32_t num_tokens, int32_t num_q_heads,
+                              int32_t head_size, void *out, int32_t out_dtype,
+                              int64_t o_stride_token, int64_t o_stride_head,
+                              float *lse_out, void *stream);
+
+/* Bytes of workspace a split call needs: o_partial (fp32 [P, T, Hq, D],
+ * rounded up to 256 bytes) followed by lse_partial (fp32 [P, T, Hq]).
+ * Returns 0 when num_splits <= 1. */
+size_t ua_workspace_size(int32_t num_tokens, int32_t num_q_heads, int32_t head_size,
+                         int32_t num_splits);
+
+/* The launch ua_unified_attention would make for *p (host only, no HIP call).
+ * Validates *p exactly as ua_unified_attention does. */
+ua_status ua_plan(const ua_attn_params *p, ua_plan_info *plan);
+
+/* Static text for a status code. */
+const char *ua_status_string(int32_t status);
+
+/* UA_ABI_VERSION of the built library. */
+uint32_t ua_abi_version(void);
+
+/* sizeof(ua_attn_params) and sizeof(ua_plan_info) of the built library, so a
+ * binding can check its mirror of the structs. */
+size_t ua_params_size(void);
+size_t ua_plan_info_size(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* UA_H */

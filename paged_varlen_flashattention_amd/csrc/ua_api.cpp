@@ -1,0 +1,285 @@
+// C-ABI layer: argument validation, launch planning and kernel enqueue.
+//
+// The host side of the unified attention call (page "vLLM Triton unified
+// attention notes", section unified_attention: assertions, shape parameters,
+// num_queries_per_kv and the query-block count are derived on the host, and
+// the grid is sized there without reading device memory).  The split path
+// mirrors the two-step interface of page "flashatten takeaways EP2 工程",
+// section "源代码接口": the partial pass, then the combine on the same stream,
+// at most 128 splits.
+
+#include "ua.h"
+#include "ua_internal.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+namespace {
+
+using ua::Tile;
+
+constexpr int kMaxSplits = 128;
+constexpr int kMaxGroup = 128;
+constexpr size_t kAlign = 256;
+constexpr int kNumCUs = 256;
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+bool pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+int ilog2(int64_t x) {
+    int r = 0;
+    while ((int64_t(1) << r) < x)
+        ++r;
+    return r;
+}
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+size_t partial_o_bytes(int64_t T, int64_t Hq, int64_t D, int64_t P) {
+    return round_up((size_t)(P * T * Hq * D) * sizeof(float), kAlign);
+}
+
+// Checks of ua_attn_params that need no device access.  The order fixes which
+// status a call with several faults gets: ABI, sizes, dtypes, shapes,
+// pointers, strides, splits, workspace.
+ua_status validate(const ua_attn_params *p) {
+    if (p == nullptr || p->abi_version != UA_ABI_VERSION)
+        return UA_ERR_INVALID_ARG;
+    if (p->num_seqs < 0 || p->num_tokens < 0)
+        return UA_ERR_INVALID_ARG;
+    if (p->num_splits < 0 || p->num_splits > kMaxSplits)
+        return UA_ERR_INVALID_ARG;
+    if (p->num_seqs == 0 || p->num_tokens == 0)
+        return UA_OK;                                          // nothing to do
+    if (p->q_dtype != UA_BF16 && p->q_dtype != UA_FP16)
+        return p->q_dtype == UA_FP8_E4M3FN ? UA_ERR_UNSUPPORTED : UA_ERR_INVALID_ARG;
+    if (p->kv_dtype != UA_BF16 && p->kv_dtype != UA_FP16 && p->kv_dtype != UA_FP8_E4M3FN)
+        return UA_ERR_INVALID_ARG;
+    if (p->kv_dtype != p->q_dtype && p->kv_dtype != UA_FP8_E4M3FN)
+        return UA_ERR_UNSUPPORTED;                             // e.g. bf16 q with fp16 cache
+    if (p->head_size <= 0 || p->num_q_heads <= 0 || p->num_kv_heads <= 0 || p->block_size <= 0 ||
+        p->num_blocks <= 0 || p->block_table_stride <= 0 || p->max_seqlen_q < 0 || p->max_seqlen_k < 0)
+        return UA_ERR_INVALID_ARG;
+    if (p->head_size != ua::kHeadSize)
+        return UA_ERR_UNSUPPORTED;
+    if (p->num_q_heads % p->num_kv_heads != 0)
+        return UA_ERR_INVALID_ARG;
+    if (p->num_q_heads / p->num_kv_heads > kMaxGroup)
+        return UA_ERR_UNSUPPORTED;
+    if (!pow2(p->block_size) || p->block_size < 16 || p->block_size > 4096)
+        return UA_ERR_UNSUPPORTED;
+    if ((int64_t)p->block_table_stride * p->block_size < p->max_seqlen_k)
+        return UA_ERR_INVALID_ARG;                             // table too narrow for max_seqlen_k
+    if (!(std::isfinite(p->softmax_scale) && p->softmax_scale > 0.0f))
+        return UA_ERR_INVALID_ARG;
+    if (p->causal != 0 && p->causal != 1)
+        return UA_ERR_INVALID_ARG;
+    if (!p->q || !p->k_cache || !p->v_cache || !p->out || !p->cu_seqlens_q || !p->seqused_k ||
+        !p->block_table)
+        return UA_ERR_INVALID_ARG;
+    if (!aligned(p->q, 16) || !aligned(p->k_cache, 16) || !aligned(p->v_cache, 16) ||
+        !aligned(p->out, 16) || !aligned(p->cu_seqlens_q, 4) || !aligned(p->seqused_k, 4) ||
+        !aligned(p->block_table, 4) || !aligned(p->lse_out, 4))
+        return UA_ERR_INVALID_ARG;
+    if (p->kv_dtype == UA_FP8_E4M3FN &&
+        (!p->k_scale || !p->v_scale || !aligned(p->k_scale, 4) || !aligned(p->v_scale, 4)))
+        return UA_ERR_INVALID_ARG;
+    const int64_t strides[] = {p->q_stride_token, p->q_stride_head, p->o_stride_token,
+                               p->o_stride_head, p->kv_stride_block, p->kv_stride_slot,
+                               p->kv_stride_head};
+    for (int64_t st : strides)
+        if (st <= 0 || st % 8 != 0)
+            return UA_ERR_INVALID_ARG;
+    return UA_OK;
+}
+
+struct Plan {
+    Tile tile;
+    ua::TileShape shape;
+    int32_t block_q;
+    int32_t splits;
+    int64_t qslots;
+};
+
+// Tile choice: the decode tile (1 wave, 32 rows, 32-key tiles) when every
+// query block fits 32 rows; else the prefill tile (4 waves, 128 rows, 64-key
+// tiles).  Split choice for num_splits = 0: enough workgroups for about two
+// rounds over the CUs, each split keeping at least 8 key tiles, within what
+// the workspace holds.
+Plan make_plan(const ua_attn_params *p) {
+    Plan pl;
+    const int G = p->num_q_heads / p->num_kv_heads;
+    pl.tile = ((int64_t)p->max_seqlen_q * G <= 32) ? Tile::Decode : Tile::Prefill;
+    pl.shape = ua::tile_shape(pl.tile);
+    if (G > pl.shape.block_m) {
+        pl.tile = Tile::Prefill;
+        pl.shape = ua::tile_shape(pl.tile);
+    }
+    pl.block_q = pl.shape.block_m / G;
+    pl.qslots = (int64_t)p->num_tokens / pl.block_q + p->num_seqs;
+    int splits = p->num_splits;
+    if (splits == 0) {
+        const int64_t blocks_per_seq =
+            ((int64_t)p->max_seqlen_q + pl.block_q - 1) / pl.block_q;
+        int64_t units = std::min<int64_t>(pl.qslots, p->num_seqs * std::max<int64_t>(blocks_per_seq, 1)) *
+                        p->num_kv_heads;
+        const int64_t waves_wanted = 2LL * kNumCUs * 8;        // two rounds at 8 waves per CU
+        const int64_t wg_wanted = waves_wanted / pl.shape.num_waves;
+        int64_t want = units > 0 ? (wg_wanted + units - 1) / units : 1;
+        const int64_t max_by_len = std::max<int64_t>(1, p->max_seqlen_k / (8 * pl.shape.tile_n));
+        want = std::min<int64_t>({want, max_by_len, (int64_t)kMaxSplits});
+        splits = (int)std::max<int64_t>(1, want);
+        while (splits > 1 && ua_workspace_size(p->num_tokens, p->num_q_heads, p->head_size, splits) >
+                                 (p->workspace ? p->workspace_bytes : 0))
+            --splits;
+    }
+    pl.splits = std::max(1, splits);
+    return pl;
+}
+
+}  // namespace
+
+extern "C" {
+
+uint32_t ua_abi_version(void) { return UA_ABI_VERSION; }
+size_t ua_params_size(void) { return sizeof(ua_attn_params); }
+size_t ua_plan_info_size(void) { return sizeof(ua_plan_info); }
+
+const char *ua_status_string(int32_t status) {
+    switch (status) {
+    case UA_OK: return "ok";
+    case UA_ERR_INVALID_ARG: return "invalid argument";
+    case UA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case UA_ERR_WORKSPACE: return "workspace missing or too small for the requested splits";
+    case UA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+size_t ua_workspace_size(int32_t num_tokens, int32_t num_q_heads, int32_t head_size,
+                         int32_t num_splits) {
+    if (num_splits <= 1 || num_tokens <= 0 || num_q_heads <= 0 || head_size <= 0)
+        return 0;
+    return partial_o_bytes(num_tokens, num_q_heads, head_size, num_splits) +
+           round_up((size_t)num_splits * num_tokens * num_q_heads * sizeof(float), kAlign);
+}
+
+ua_status ua_plan(const ua_attn_params *p, ua_plan_info *plan) {
+    if (plan == nullptr)
+        return UA_ERR_INVALID_ARG;
+    std::memset(plan, 0, sizeof(*plan));
+    const ua_status st = validate(p);
+    if (st != UA_OK)
+        return st;
+    if (p->num_seqs == 0 || p->num_tokens == 0)
+        return UA_OK;
+    const Plan pl = make_plan(p);
+    if (pl.splits > 1) {
+        const size_t need = ua_workspace_size(p->num_tokens, p->num_q_heads, p->head_size, pl.splits);
+        if (!p->workspace || !aligned(p->workspace, kAlign) || p->workspace_bytes < need)
+            return UA_ERR_WORKSPACE;
+    }
+    plan->block_m = pl.shape.block_m;
+    plan->block_q = pl.block_q;
+    plan->tile_n = pl.shape.tile_n;
+    plan->num_waves = pl.shape.num_waves;
+    plan->num_splits = pl.splits;
+    plan->grid_x = pl.qslots * p->num_kv_heads;
+    plan->grid_y = pl.splits;
+    return UA_OK;
+}
+
+ua_status ua_unified_attention(const ua_attn_params *p, void *stream) {
+    ua_plan_info info;
+    const ua_status st = ua_plan(p, &info);
+    if (st != UA_OK)
+        return st;
+    if (p->num_seqs == 0 || p->num_tokens == 0)
+        return UA_OK;
+    if (info.grid_x > 0x7fffffff)
+        return UA_ERR_UNSUPPORTED;
+    const Plan pl = make_plan(p);
+    const bool split = pl.splits > 1;
+    const int G = p->num_q_heads / p->num_kv_heads;
+
+    ua::AttnArgs a{};
+    a.q = p->q;
+    a.k = p->k_cache;
+    a.v = p->v_cache;
+    a.out = p->out;
+    a.cu_seqlens_q = p->cu_seqlens_q;
+    a.seqused_k = p->seqused_k;
+    a.block_table = p->block_table;
+    a.k_scale = p->kv_dtype == UA_FP8_E4M3FN ? p->k_scale : nullptr;
+    a.v_scale = p->kv_dtype == UA_FP8_E4M3FN ? p->v_scale : nullptr;
+    a.lse_out = split ? nullptr : p->lse_out;
+    if (split) {
+        uint8_t *ws = static_cast<uint8_t *>(p->workspace);
+        a.o_part = reinterpret_cast<float *>(ws);
+        a.lse_part = reinterpret_cast<float *>(
+            ws + partial_o_bytes(p->num_tokens, p->num_q_heads, p->head_size, pl.splits));
+    }
+    a.q_st_tok = p->q_stride_token;
+    a.q_st_head = p->q_stride_head;
+    a.o_st_tok = p->o_stride_token;
+    a.o_st_head = p->o_stride_head;
+    a.kv_st_blk = p->kv_stride_block;
+    a.kv_st_slot = p->kv_stride_slot;
+    a.kv_st_head = p->kv_stride_head;
+    a.bt_stride = p->block_table_stride;
+    a.num_seqs = p->num_seqs;
+    a.num_tokens = p->num_tokens;
+    a.num_q_heads = p->num_q_heads;
+    a.num_kv_heads = p->num_kv_heads;
+    a.group = G;
+    a.block_q = pl.block_q;
+    a.log2_block_size = ilog2(p->block_size);
+    a.num_splits = pl.splits;
+    a.num_qslots = (int32_t)pl.qslots;
+    a.scale_log2 = p->softmax_scale * 1.44269504088896341f;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const dim3 grid((unsigned)info.grid_x, (unsigned)info.grid_y);
+    if (ua::launch_attention(a, pl.tile, p->q_dtype == UA_FP16, p->kv_dtype == UA_FP8_E4M3FN,
+                             p->causal != 0, split, grid, s) != hipSuccess)
+        return UA_ERR_HIP;
+    if (split) {
+        if (ua::launch_combine(a.o_part, a.lse_part, pl.splits,
+                               (int64_t)p->num_tokens * p->num_q_heads, p->num_q_heads, p->out,
+                               p->q_dtype == UA_FP16, p->o_stride_token, p->o_stride_head,
+                               p->lse_out, s) != hipSuccess)
+            return UA_ERR_HIP;
+    }
+    return UA_OK;
+}
+
+ua_status ua_split_kv_combine(const float *o_partial, const float *lse_partial, int32_t num_splits,
+                              int32_t num_tokens, int32_t num_q_heads, int32_t head_size,
+                              void *out, int32_t out_dtype, int64_t o_stride_token,
+                              int64_t o_stride_head, float *lse_out, void *stream) {
+    if (num_splits < 1 || num_splits > kMaxSplits || num_tokens < 0 || num_q_heads <= 0)
+        return UA_ERR_INVALID_ARG;
+    if (out_dtype != UA_BF16 && out_dtype != UA_FP16)
+        return out_dtype == UA_FP8_E4M3FN ? UA_ERR_UNSUPPORTED : UA_ERR_INVALID_ARG;
+    if (head_size <= 0)
+        return UA_ERR_INVALID_ARG;
+    if (head_size != ua::kHeadSize)
+        return UA_ERR_UNSUPPORTED;
+    if (num_tokens == 0)
+        return UA_OK;
+    if (!o_partial || !lse_partial || !out)
+        return UA_ERR_INVALID_ARG;
+    if (!aligned(o_partial, 16) || !aligned(lse_partial, 4) || !aligned(out, 16) || !aligned(lse_out, 4))
+        return UA_ERR_INVALID_ARG;
+    if (o_stride_token <= 0 || o_stride_head <= 0 || o_stride_token % 8 || o_stride_head % 8)
+        return UA_ERR_INVALID_ARG;
+    if (ua::launch_combine(o_partial, lse_partial, num_splits, (int64_t)num_tokens * num_q_heads,
+                           num_q_heads, out, out_dtype == UA_FP16, o_stride_token, o_stride_head,
+                           lse_out, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return UA_ERR_HIP;
+    return UA_OK;
+}
+
+}  // extern "C"

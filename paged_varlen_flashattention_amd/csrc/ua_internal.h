@@ -1,0 +1,66 @@
+// Internal interface between the C-ABI layer (ua_api.cpp) and the kernels
+// (ua_attention.hip).  Not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ua {
+
+constexpr int kHeadSize = 128;
+
+// Arguments of the attention kernel, passed by value.
+struct AttnArgs {
+    const void *q;
+    const void *k;
+    const void *v;
+    void *out;
+    const int32_t *cu_seqlens_q;
+    const int32_t *seqused_k;
+    const int32_t *block_table;
+    const float *k_scale;          // fp8 KV only
+    const float *v_scale;
+    float *lse_out;                // [T, Hq] or null (unsplit launches only)
+    float *o_part;                 // [P, T, Hq, D] (split launches only)
+    float *lse_part;               // [P, T, Hq]
+    int64_t q_st_tok, q_st_head;
+    int64_t o_st_tok, o_st_head;
+    int64_t kv_st_blk, kv_st_slot, kv_st_head;
+    int64_t bt_stride;
+    int32_t num_seqs, num_tokens, num_q_heads, num_kv_heads;
+    int32_t group;                 // Hq / Hkv
+    int32_t block_q;               // query tokens per workgroup
+    int32_t log2_block_size;
+    int32_t num_splits;
+    int32_t num_qslots;            // T / block_q + S
+    float scale_log2;              // softmax_scale * log2(e)
+};
+
+// A compiled tile shape of the attention kernel.
+enum class Tile : int {
+    Prefill = 0,   // 4 waves x 32 query rows, 64-key tiles
+    Decode = 1,    // 1 wave x 32 query rows, 32-key tiles
+};
+
+struct TileShape {
+    int num_waves;
+    int block_m;
+    int tile_n;
+};
+
+inline TileShape tile_shape(Tile t) {
+    return t == Tile::Prefill ? TileShape{4, 128, 64} : TileShape{1, 32, 32};
+}
+
+// Enqueue the attention kernel.  q_f16: q/out are fp16 (else bf16); kv_fp8:
+// the cache holds fp8 e4m3fn codes (else the q dtype).
+hipError_t launch_attention(const AttnArgs &a, Tile tile, bool q_f16, bool kv_fp8, bool causal,
+                            bool split, dim3 grid, hipStream_t stream);
+
+// Enqueue the split combine kernel over rows = T * Hq rows.
+hipError_t launch_combine(const float *o_part, const float *lse_part, int32_t num_splits,
+                          int64_t rows, int32_t num_q_heads, void *out, bool out_f16,
+                          int64_t o_st_tok, int64_t o_st_head, float *lse_out,
+                          hipStream_t stream);
+
+}  // namespace ua

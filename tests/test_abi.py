@@ -1,0 +1,229 @@
+"""The C-ABI library on the host: it loads, exports every symbol include/ua.h
+declares, its structs match the binding, and every host-checkable violation
+returns its documented status before any HIP call (ua_plan and the error paths
+of ua_unified_attention / ua_split_kv_combine never touch a device, so fake,
+never-dereferenced addresses are safe here).  CPU only."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import paged_varlen_flashattention_amd as ua
+from paged_varlen_flashattention_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ua.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH),
+                                reason="libua.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ua_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return ua.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    decl = declared_functions()
+    assert decl, "no declarations parsed"
+    assert sorted(ua.EXPORTS) == decl
+    for name in decl:
+        assert hasattr(lib, name), name
+
+
+def test_struct_layout(lib):
+    assert lib.ua_params_size() == ctypes.sizeof(B.AttnParams) == 216
+    assert lib.ua_plan_info_size() == ctypes.sizeof(B.PlanInfo)
+    assert lib.ua_abi_version() == B.ABI_VERSION
+
+
+def test_status_strings(lib):
+    for st in (0, -1, -2, -3, -4):
+        assert lib.ua_status_string(st)
+    assert lib.ua_status_string(12345) == b"unknown status"
+
+
+FAKE = 1 << 20   # 16-byte (and 256-byte) aligned fake device address
+
+
+def base_params(**kw):
+    """A valid parameter set for config-3-like shapes with fake addresses."""
+    p = B.AttnParams()
+    p.abi_version = B.ABI_VERSION
+    p.q_dtype = p.kv_dtype = B.UA_BF16
+    p.causal = 1
+    for name in ("q", "k_cache", "v_cache", "out", "cu_seqlens_q", "seqused_k", "block_table"):
+        setattr(p, name, FAKE)
+    S, Hq, Hkv, D, bs = 256, 32, 8, 128, 16
+    p.num_seqs, p.num_tokens, p.num_q_heads, p.num_kv_heads = S, S, Hq, Hkv
+    p.head_size, p.block_size, p.num_blocks, p.block_table_stride = D, bs, 65536, 512
+    p.q_stride_token, p.q_stride_head = Hq * D, D
+    p.o_stride_token, p.o_stride_head = Hq * D, D
+    p.kv_stride_block, p.kv_stride_slot, p.kv_stride_head = bs * Hkv * D, Hkv * D, D
+    p.max_seqlen_q, p.max_seqlen_k = 1, 8192
+    p.num_splits = 1
+    p.softmax_scale = 1 / math.sqrt(128)
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def plan_status(lib, p):
+    info = B.PlanInfo()
+    return lib.ua_plan(ctypes.byref(p), ctypes.byref(info)), info
+
+
+def test_valid_plan_decode(lib):
+    st, info = plan_status(lib, base_params())
+    assert st == 0
+    # decode tile: 32 rows = 8 tokens x G=4 heads; slots = T/8 + S = 32 + 256
+    assert (info.block_m, info.block_q, info.tile_n, info.num_waves) == (32, 8, 32, 1)
+    assert info.grid_x == (256 // 8 + 256) * 8 and info.grid_y == 1
+
+
+def test_valid_plan_prefill(lib):
+    p = base_params(num_seqs=4, num_tokens=16384, num_q_heads=32, num_kv_heads=32,
+                    max_seqlen_q=4096, max_seqlen_k=4096, block_table_stride=256,
+                    q_stride_token=32 * 128, o_stride_token=32 * 128,
+                    kv_stride_block=16 * 32 * 128, kv_stride_slot=32 * 128)
+    st, info = plan_status(lib, p)
+    assert st == 0
+    assert (info.block_m, info.block_q, info.tile_n, info.num_waves) == (128, 128, 64, 4)
+    assert info.grid_x == (16384 // 128 + 4) * 32
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("abi_version", 7, B.UA_ERR_INVALID_ARG),
+    ("num_seqs", -1, B.UA_ERR_INVALID_ARG),
+    ("num_tokens", -5, B.UA_ERR_INVALID_ARG),
+    ("num_splits", 129, B.UA_ERR_INVALID_ARG),
+    ("num_splits", -1, B.UA_ERR_INVALID_ARG),
+    ("q_dtype", B.UA_FP8_E4M3FN, B.UA_ERR_UNSUPPORTED),
+    ("q_dtype", 9, B.UA_ERR_INVALID_ARG),
+    ("kv_dtype", B.UA_FP16, B.UA_ERR_UNSUPPORTED),
+    ("kv_dtype", 9, B.UA_ERR_INVALID_ARG),
+    ("head_size", 64, B.UA_ERR_UNSUPPORTED),
+    ("head_size", 0, B.UA_ERR_INVALID_ARG),
+    ("num_q_heads", 30, B.UA_ERR_INVALID_ARG),        # 30 % 8 != 0
+    ("num_kv_heads", 0, B.UA_ERR_INVALID_ARG),
+    ("block_size", 24, B.UA_ERR_UNSUPPORTED),
+    ("block_size", 8, B.UA_ERR_UNSUPPORTED),
+    ("block_size", 8192, B.UA_ERR_UNSUPPORTED),
+    ("block_table_stride", 100, B.UA_ERR_INVALID_ARG),  # 100 * 16 < 8192
+    ("softmax_scale", 0.0, B.UA_ERR_INVALID_ARG),
+    ("softmax_scale", -0.1, B.UA_ERR_INVALID_ARG),
+    ("softmax_scale", float("nan"), B.UA_ERR_INVALID_ARG),
+    ("softmax_scale", float("inf"), B.UA_ERR_INVALID_ARG),
+    ("causal", 2, B.UA_ERR_INVALID_ARG),
+    ("q", None, B.UA_ERR_INVALID_ARG),
+    ("k_cache", None, B.UA_ERR_INVALID_ARG),
+    ("v_cache", None, B.UA_ERR_INVALID_ARG),
+    ("out", None, B.UA_ERR_INVALID_ARG),
+    ("cu_seqlens_q", None, B.UA_ERR_INVALID_ARG),
+    ("seqused_k", None, B.UA_ERR_INVALID_ARG),
+    ("block_table", None, B.UA_ERR_INVALID_ARG),
+    ("q", FAKE + 8, B.UA_ERR_INVALID_ARG),             # not 16-byte aligned
+    ("out", FAKE + 2, B.UA_ERR_INVALID_ARG),
+    ("k_cache", FAKE + 4, B.UA_ERR_INVALID_ARG),
+    ("lse_out", FAKE + 2, B.UA_ERR_INVALID_ARG),
+    ("q_stride_head", 100, B.UA_ERR_INVALID_ARG),      # not a multiple of 8
+    ("o_stride_token", 0, B.UA_ERR_INVALID_ARG),
+    ("kv_stride_slot", -1024, B.UA_ERR_INVALID_ARG),
+    ("max_seqlen_q", -1, B.UA_ERR_INVALID_ARG),
+])
+def test_invalid_arguments(lib, field, value, status):
+    p = base_params(**{field: value})
+    st, info = plan_status(lib, p)
+    assert st == status
+    assert info.grid_x == 0
+    # the launch entry point rejects the same call before touching HIP
+    assert lib.ua_unified_attention(ctypes.byref(p), None) == status
+
+
+def test_fp8_requires_scales(lib):
+    p = base_params(kv_dtype=B.UA_FP8_E4M3FN)
+    assert plan_status(lib, p)[0] == B.UA_ERR_INVALID_ARG
+    p = base_params(kv_dtype=B.UA_FP8_E4M3FN, k_scale=FAKE, v_scale=FAKE)
+    assert plan_status(lib, p)[0] == B.UA_OK
+
+
+def test_split_needs_workspace(lib):
+    need = lib.ua_workspace_size(256, 32, 128, 8)
+    assert need == 8 * 256 * 32 * 128 * 4 + 8 * 256 * 32 * 4
+    assert plan_status(lib, base_params(num_splits=8))[0] == B.UA_ERR_WORKSPACE
+    p = base_params(num_splits=8, workspace=FAKE, workspace_bytes=need - 1)
+    assert plan_status(lib, p)[0] == B.UA_ERR_WORKSPACE
+    p = base_params(num_splits=8, workspace=FAKE + 16, workspace_bytes=need)
+    assert plan_status(lib, p)[0] == B.UA_ERR_WORKSPACE          # not 256-byte aligned
+    p = base_params(num_splits=8, workspace=FAKE, workspace_bytes=need)
+    st, info = plan_status(lib, p)
+    assert st == 0 and info.num_splits == 8 and info.grid_y == 8
+    assert lib.ua_unified_attention(ctypes.byref(base_params(num_splits=8)), None) == B.UA_ERR_WORKSPACE
+
+
+def test_auto_splits_respect_workspace(lib):
+    st, info = plan_status(lib, base_params(num_splits=0))
+    assert st == 0 and info.num_splits == 1                        # no workspace: no split
+    p = base_params(num_splits=0, workspace=FAKE, workspace_bytes=1 << 40)
+    st, info = plan_status(lib, p)
+    assert st == 0 and 1 < info.num_splits <= 128
+    small = lib.ua_workspace_size(256, 32, 128, 2)
+    p = base_params(num_splits=0, workspace=FAKE, workspace_bytes=small)
+    st, info = plan_status(lib, p)
+    assert st == 0 and info.num_splits == 2
+
+
+def test_workspace_size_edges(lib):
+    assert lib.ua_workspace_size(256, 32, 128, 1) == 0
+    assert lib.ua_workspace_size(0, 32, 128, 4) == 0
+    assert lib.ua_workspace_size(17, 64, 128, 32) % 256 == 0
+
+
+def test_empty_batch_is_noop(lib):
+    p = base_params(num_seqs=0, q=None)
+    assert plan_status(lib, p)[0] == B.UA_OK
+    assert lib.ua_unified_attention(ctypes.byref(p), None) == B.UA_OK
+    p = base_params(num_tokens=0, q=None)
+    assert lib.ua_unified_attention(ctypes.byref(p), None) == B.UA_OK
+
+
+def test_null_params(lib):
+    info = B.PlanInfo()
+    assert lib.ua_plan(None, ctypes.byref(info)) == B.UA_ERR_INVALID_ARG
+    assert lib.ua_plan(ctypes.byref(base_params()), None) == B.UA_ERR_INVALID_ARG
+    assert lib.ua_unified_attention(None, None) == B.UA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(num_splits=0), B.UA_ERR_INVALID_ARG),
+    (dict(num_splits=129), B.UA_ERR_INVALID_ARG),
+    (dict(head_size=64), B.UA_ERR_UNSUPPORTED),
+    (dict(out_dtype=B.UA_FP8_E4M3FN), B.UA_ERR_UNSUPPORTED),
+    (dict(out_dtype=7), B.UA_ERR_INVALID_ARG),
+    (dict(o_partial=None), B.UA_ERR_INVALID_ARG),
+    (dict(out=FAKE + 4), B.UA_ERR_INVALID_ARG),
+    (dict(o_stride_head=12), B.UA_ERR_INVALID_ARG),
+    (dict(num_tokens=0, o_partial=None), B.UA_OK),
+])
+def test_combine_invalid_arguments(lib, args, status):
+    a = dict(o_partial=FAKE, lse_partial=FAKE, num_splits=4, num_tokens=17, num_q_heads=64,
+             head_size=128, out=FAKE, out_dtype=B.UA_BF16, o_stride_token=64 * 128,
+             o_stride_head=128, lse_out=None)
+    a.update(args)
+    st = lib.ua_split_kv_combine(a["o_partial"], a["lse_partial"], a["num_splits"], a["num_tokens"],
+                                 a["num_q_heads"], a["head_size"], a["out"], a["out_dtype"],
+                                 a["o_stride_token"], a["o_stride_head"], a["lse_out"], None)
+    assert st == status
+
+
+def test_binding_raises_without_library(tmp_path):
+    with pytest.raises(RuntimeError, match="missing"):
+        B.load_library(str(tmp_path / "nope.so"))

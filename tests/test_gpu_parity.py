@@ -1,0 +1,212 @@
+"""Parity of the HIP path (called through the C ABI) with the CPU fp64 oracle.
+
+Tolerances: max abs error <= 2e-2 for bf16/fp16 caches, <= 6e-2 for fp8 e4m3fn
+caches (bf16/fp16 inputs, fp32 accumulation); natural-log LSE within 1e-3.
+Small and medium cases are compared on every output row; the full-size dense
+and mixed batches on sampled rows (sequence ends, block boundaries, random
+picks) that the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gpu_helpers as H
+import oracle
+import workloads as wk
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="no GPU")]
+
+
+# ------------------------------------------------------------------ the five workloads
+
+def test_config1_tiny_paged_varlen():
+    wl = wk.config1()
+    H.say("config1 tiny paged varlen")
+    out, lse = H.run(wl)
+    H.compare(wl, out, lse, what="config1")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_config2_dense_reduced_all_rows(causal):
+    wl = wk.config2(causal=causal, batch=2, heads=4, seq=640)
+    H.say(f"config2 reduced causal={causal}")
+    out, lse = H.run(wl)
+    H.compare(wl, out, lse, what="config2 reduced")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_config2_dense_full_size_sampled(causal):
+    wl = wk.config2(causal=causal)
+    H.say(f"config2 full size causal={causal}")
+    out, lse = H.run(wl)
+    rows = H.sample_rows(wl, 600, seed=2)
+    H.compare(wl, out, lse, rows=rows, what="config2 full")
+
+
+@pytest.fixture(scope="module")
+def c3():
+    wl = wk.config3()
+    ref = oracle.attention_workload(wl)
+    return wl, H.to_device(wl), ref
+
+
+@pytest.mark.parametrize("splits", [1, 2, 4, 8])
+def test_config3_decode_splits(c3, splits):
+    wl, dev, (ref, ref_lse) = c3
+    H.say(f"config3 decode splits={splits}")
+    out, lse = H.run(wl, dev, num_splits=splits)
+    g = H.out_f64(out)
+    err = np.abs(g - ref).max()
+    assert np.all(np.isfinite(g)) and err <= 2e-2, err
+    lerr = np.abs(lse.cpu().numpy() - ref_lse).max()
+    assert lerr <= H.LSE_TOL, lerr
+
+
+def test_config4_mixed_chunked_prefill():
+    wl = wk.config4()
+    H.say("config4 mixed chunked prefill")
+    out, lse = H.run(wl)
+    decode_rows = np.array([(t, h) for t in range(64) for h in range(wl.num_q_heads)])
+    H.compare(wl, out, lse, rows=decode_rows, what="config4 decode rows")
+    rows = H.sample_rows(wl, 500, seed=4)
+    rows = rows[rows[:, 0] >= 64]
+    H.compare(wl, out, lse, rows=rows, what="config4 prefill rows")
+
+
+def test_config5_long_context_fp8_32_splits():
+    wl = wk.config5()
+    H.say("config5 long context fp8 32 splits")
+    out, lse = H.run(wl, num_splits=32)
+    rows = np.array([(0, h) for h in range(0, 64, 4)] + [(t, (7 * t) % 64) for t in range(1, 17)]
+                    + [(16, h) for h in range(0, 64, 9)])
+    H.compare(wl, out, lse, rows=rows, what="config5")
+
+
+# ------------------------------------------------------------------ sweeps and edge cases
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_moderate_shapes(seed):
+    kind = seed % 6
+    kw = dict(max_seqs=5, max_kv=700)
+    if kind == 1:
+        kw.update(heads=(8, 2))
+    elif kind == 2:
+        kw.update(heads=(16, 1), dtype="fp16")
+    elif kind == 3:
+        kw.update(heads=(8, 8), kv_dtype="fp8_e4m3fn")
+    elif kind == 4:
+        kw.update(heads=(6, 2))                      # G = 3: rows do not fill the tile
+    elif kind == 5:
+        kw.update(heads=(4, 1), block_size=64, dtype="fp16", kv_dtype="fp8_e4m3fn")
+    wl = wk.random_small(100 + seed, **kw)
+    H.say(f"random seed={seed} q={wl.q_lens.tolist()} kv={wl.kv_lens.tolist()} causal={wl.causal}")
+    out, lse = H.run(wl)
+    H.compare(wl, out, lse, what=f"random {seed}")
+
+
+@pytest.mark.parametrize("q_lens,kv_lens,heads,bs", [
+    ([1], [1], (4, 4), 16),                          # one key
+    ([1, 0, 1], [1, 5, 17], (8, 2), 16),             # empty query sequence in the middle
+    ([16, 17, 15], [16, 17, 15], (4, 4), 16),        # kv = block_size and +-1
+    ([0, 3], [40, 3], (2, 1), 32),
+    ([130, 1], [300, 257], (2, 2), 16),              # q crosses a 128-token block
+    ([2], [100], (64, 1), 16),                       # G = 64
+    ([1], [65], (128, 1), 16),                       # G = 128, one token per block
+    ([33], [33], (1, 1), 32),                        # decode-tile boundary
+])
+@pytest.mark.parametrize("causal", [True, False])
+def test_edge_shapes(q_lens, kv_lens, heads, bs, causal):
+    wl = wk.make_paged("edge", 4000 + len(q_lens) + bs, q_lens, kv_lens, heads[0], heads[1],
+                       block_size=bs, causal=causal)
+    H.say(f"edge q={q_lens} kv={kv_lens} heads={heads} bs={bs} causal={causal}")
+    out, lse = H.run(wl)
+    H.compare(wl, out, lse, what="edge")
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 5, 8, 32, 0])
+def test_split_counts(splits):
+    wl = wk.make_paged("splits", 4100, [1, 9, 1, 70], [900, 500, 64, 1000], 8, 2,
+                       block_size=16, causal=True)
+    H.say(f"splits={splits}")
+    out, lse = H.run(wl, num_splits=splits)
+    H.compare(wl, out, lse, what=f"splits {splits}")
+
+
+def test_page_relabel_is_bitwise_invariant():
+    wl = wk.make_paged("relabel", 4200, [3, 40, 1], [300, 200, 77], 8, 2, block_size=16, causal=True)
+    H.say("page relabel")
+    out1, lse1 = H.run(wl)
+    pi = torch.from_numpy(np.random.default_rng(3).permutation(wl.num_blocks))
+    k2 = torch.empty_like(wl.k_cache); k2[pi] = wl.k_cache
+    v2 = torch.empty_like(wl.v_cache); v2[pi] = wl.v_cache
+    wl2 = wk.Workload(**{**wl.__dict__, "k_cache": k2, "v_cache": v2,
+                         "block_table": pi[wl.block_table.long()].to(torch.int32)})
+    out2, lse2 = H.run(wl2)
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(lse1, lse2)
+
+
+def test_poisoned_unused_table_entries():
+    kw = dict(block_size=16, causal=True, width=64)
+    wl = wk.make_paged("poison", 4300, [5, 1], [70, 33], 4, 4, **kw)
+    wl_p = wk.make_paged("poison", 4300, [5, 1], [70, 33], 4, 4, poison_unused=True, **kw)
+    assert (wl_p.block_table == -1).any()
+    H.say("poisoned table")
+    out1, _ = H.run(wl)
+    out2, _ = H.run(wl_p)
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+
+
+def test_deterministic():
+    wl = wk.make_paged("det", 4400, [1, 64, 200], [1000, 300, 200], 8, 2, block_size=32, causal=True)
+    H.say("determinism")
+    d = H.to_device(wl)
+    a, la = H.run(wl, d, num_splits=4)
+    b, lb = H.run(wl, d, num_splits=4)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16)) and torch.equal(la, lb)
+
+
+def test_strided_q_and_out_with_guard_canaries():
+    """q is a view into a packed qkv tensor; out sits inside a larger buffer whose
+    guard regions must stay untouched."""
+    wl = wk.make_paged("strided", 4500, [7, 1, 30], [50, 20, 30], 8, 2, block_size=16, causal=True)
+    H.say("strided q / out with canaries")
+    T, Hq, D = wl.q.shape
+    qkv = torch.zeros(T, 3 * Hq, D, dtype=wl.q.dtype)
+    qkv[:, Hq:2 * Hq] = wl.q
+    d = H.to_device(wl)
+    d["q"] = qkv.cuda()[:, Hq:2 * Hq]
+    big = torch.full((T + 2, 2 * Hq, D), 7.0, dtype=wl.q.dtype, device="cuda")
+    out = big[1:T + 1, 3:3 + Hq]
+    out.fill_(float("nan"))
+    out, lse = H.run(wl, d, out=out)
+    H.compare(wl, out, lse, what="strided")
+    mask = torch.ones_like(big, dtype=torch.bool)
+    mask[1:T + 1, 3:3 + Hq] = False
+    assert torch.all(big[mask] == 7.0), "write outside out"
+
+
+@pytest.mark.parametrize("P", [1, 3, 32, 128])
+def test_combine_kernel_against_oracle(P):
+    rng = np.random.default_rng(P)
+    T, Hq, D = 9, 8, 128
+    o = rng.standard_normal((P, T, Hq, D)).astype(np.float32)
+    lse = (rng.standard_normal((P, T, Hq)) * 3).astype(np.float32)
+    lse[rng.random((P, T, Hq)) < 0.3] = -np.inf        # empty splits
+    lse[:, 0, 0] = -np.inf                              # a row with every split empty
+    H.say(f"combine P={P}")
+    out = torch.full((T, Hq, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse_out = torch.full((T, Hq), float("nan"), dtype=torch.float32, device="cuda")
+    import paged_varlen_flashattention_amd as ua
+    ua.split_kv_combine(torch.from_numpy(o).cuda(), torch.from_numpy(lse).cuda(), out, lse_out)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.combine(o.reshape(P, T * Hq, D).astype(np.float64),
+                                  lse.reshape(P, T * Hq).astype(np.float64))
+    got = H.out_f64(out).reshape(T * Hq, D)
+    assert np.abs(got - ref).max() <= 2e-2
+    gl = lse_out.cpu().numpy().reshape(-1).astype(np.float64)
+    assert np.array_equal(np.isneginf(gl), np.isneginf(ref_lse))
+    fin = np.isfinite(ref_lse)
+    assert np.abs(gl[fin] - ref_lse[fin]).max() <= 1e-4
+    assert np.all(got[0] == 0.0)
