@@ -28,7 +28,9 @@
 //     O^T = V^T P^T.
 //   * Online softmax (page "Fused Attention", FA2 tutorial listing, the inner
 //     loop): running max m and sum l in log2 units, alpha = 2^(m_old - m_new)
-//     rescales the accumulator, a single division at the end.  Tiles that
+//     rescales the accumulator, a single division at the end.  Unlike the
+//     listing, m is only moved when a tile's max exceeds it by 2^8, so most
+//     tiles skip the rescale.  Tiles that
 //     every row of the block sees in full skip the mask (the tutorial's
 //     off-band / on-band split).
 //   * Split-KV (page "flashatten takeaways EP2 工程", section "源代码接口";
@@ -49,6 +51,7 @@ namespace {
 constexpr int HD = kHeadSize;
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kLog2e = 1.44269504088896341f;
+constexpr float kRescaleLog2 = 8.0f;     // lazy-rescale threshold, log2 units
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -115,8 +118,11 @@ __device__ __forceinline__ int swz_k(int j) { return swap23(j & 15); }
 template <int VG>
 __device__ __forceinline__ int swz_v(int d) { return (d + (d >> 3)) & (VG - 1); }
 
+// Two waves per SIMD: the kernel is written to fit 256 VGPRs so that the
+// softmax of one wave overlaps the MFMAs of the other.
 template <bool F16, bool FP8KV, bool CAUSAL, bool SPLIT, int NW, int TN>
-__global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_kernel(const AttnArgs a) {
     constexpr int NT = NW * 64;                 // threads
     constexpr int NKB = TN / 32;                // 32-key blocks per tile (S^T MFMA M)
     constexpr int NPV = TN / 16;                // 16-key steps per tile (PV MFMA K)
@@ -313,9 +319,23 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const AttnArgs a) {
                 mx = fmaxf(mx, sacc[b][q]);
         mx = fmaxf(mx, __shfl_xor(mx, 32));
 
-        const float m_new = fmaxf(m, mx * c2);
-        const float m_use = (m_new == neg_inf()) ? 0.0f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m - m_use);
+        // The reference max m only moves when this tile's max exceeds it by
+        // more than kRescaleLog2 (a factor 2^8): weights 2^(s - m) then stay
+        // below 256, and the accumulator and sum are rescaled only on those
+        // (rare, after the first tiles) steps.  The final division by l makes
+        // the result independent of which reference was used.
+        const float tmax = mx * c2;
+        const bool grow = tmax > m + kRescaleLog2;          // also true for the first finite max
+        if (__ballot(grow) != 0) {
+            // rows that do not grow keep alpha = 1 (their m may still be -inf)
+            const float alpha = grow ? __builtin_amdgcn_exp2f(m - tmax) : 1.0f;  // 0 if m was -inf
+            m = grow ? tmax : m;
+            l *= alpha;
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+                o[x] *= alpha;
+        }
+        const float m_use = (m == neg_inf()) ? 0.0f : m;    // fully masked so far: weights 0
         float rs = 0.0f;
 #pragma unroll
         for (int b = 0; b < NKB; ++b)
@@ -325,11 +345,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const AttnArgs a) {
                 sacc[b][q] = p;
                 rs += p;
             }
-        l = l * alpha + rs;
-        m = m_new;
-#pragma unroll
-        for (int x = 0; x < 4; ++x)
-            o[x] *= alpha;
+        l += rs;
 
         // P (16-bit) as the B operand of O^T += V^T P^T
         u32x4 pf[NPV];
