@@ -41,7 +41,24 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the oracle CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain device copy of --copy-bytes bytes (counter calibration)")
+    ap.add_argument("--copy-bytes", type=int, default=1 << 30)
     return ap.parse_args()
+
+
+def copy_calibration(nbytes: int, reps: int = 3) -> None:
+    """A plain device-to-device copy of a known size: under rocprofv3 --pmc its
+    FETCH_SIZE / WRITE_SIZE per dispatch calibrate what those counters read per
+    byte actually moved."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "reps": reps}), flush=True)
 
 
 def kernel_source_hash() -> str:
@@ -54,16 +71,21 @@ def kernel_source_hash() -> str:
 
 
 def traffic_from_profiles(kernel_tag: str):
-    """HBM bytes per launch measured by rocprofv3 counters (profiles/traffic_*.json),
-    only while the kernel sources are unchanged since they were taken."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel_tag}.json")
+    """HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE counters
+    (profiles/traffic_<tag>.txt, counters scaled by a plain-copy calibration),
+    or None when no such record exists or the kernel sources changed since."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel_tag}.txt")
     if not os.path.exists(path):
         return None
+    rec = {}
     with open(path) as f:
-        rec = json.load(f)
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                rec[k.strip()] = v.strip()
     if rec.get("kernel_source_hash") != kernel_source_hash():
         return None
-    return rec.get("bytes_per_launch")
+    return int(float(rec["bytes_per_launch"]))
 
 
 def build_calls(cfg: str, splits_override):
@@ -92,6 +114,10 @@ def main():
                           "(the attention call has no cross-GPU step; sharding is described in "
                           "DESIGN.md)", "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_bytes)
+        return
 
     import numpy as np
     import torch
