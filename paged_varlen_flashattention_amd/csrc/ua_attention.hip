@@ -101,6 +101,12 @@ __device__ __forceinline__ u32x4 widen_fp8(u32x2 v) {
                  pack2<F16>(d[0], d[1])};
 }
 
+// A load the compiler must issue as a scalar (SMEM) load: the address is
+// uniform across the wave and the data is read-only for the kernel's lifetime.
+__device__ __forceinline__ int32_t sload(const int32_t *p) {
+    return *(const __attribute__((address_space(4))) int32_t *)p;
+}
+
 // Swap bits 2 and 3 of a row index.  K row j of a 32-key block is fed to MFMA
 // lane row swap23(j): then accumulator register r of lane half h holds key
 // 16*(r/8) + 8*h + r%8, i.e. eight consecutive keys per register octet, which
@@ -134,7 +140,9 @@ void attn_fwd_kernel(const AttnArgs a) {
     static_assert(PPT >= 1 && PAIRS % NT == 0, "tile / thread mismatch");
     using Chunk = typename std::conditional<FP8KV, u32x2, u32x4>::type;
 
-    __shared__ __attribute__((aligned(16))) uint8_t lds[TN * 256 + HD * VROW];
+    constexpr bool DB = NW > 1;                 // double-buffered LDS (prefill tile)
+    constexpr int STAGE = TN * 256 + HD * VROW; // bytes of one K + V^T stage
+    __shared__ __attribute__((aligned(16))) uint8_t lds[(DB ? 2 : 1) * STAGE];
     uint8_t *const ldsK = lds;
     uint8_t *const ldsV = lds + TN * 256;
 
@@ -206,40 +214,62 @@ void attn_fwd_kernel(const AttnArgs a) {
     }
 
     // ---------------------------------------------------------------- loader
-    // Thread unit i: key pair p = tid/16 + i*NT/16 (keys 2p, 2p+1 of the tile),
-    // d chunk c = tid%16 (d 8c .. 8c+7).  Both keys of a pair share a page
-    // (block_size is an even power of two).
+    // Thread unit i covers keys 2p, 2p+1 of the tile, p = tid/16 + i*NT/16,
+    // and the d chunk c = tid%16 (d 8c .. 8c+7).  One load instruction of a
+    // wave covers the 8-key group starting at rbase(i) = 8*wave + i*NT/8; a
+    // page holds at least 16 keys, so the page of every load is wave-uniform:
+    // its id is a scalar load of the block table and the page base is scalar
+    // arithmetic, each lane adding a fixed offset (its key in the group, its d
+    // chunk).  Page ids are fetched one tile ahead of the K/V loads that use
+    // them, so no K/V load waits on a block-table load.
     const int c = tid & 15;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const int lanep = 2 * ((tid >> 4) & 3);
     const int32_t *btrow = a.block_table + (int64_t)s * a.bt_stride;
     const int lbs = a.log2_block_size;
     const int bs_mask = (1 << lbs) - 1;
-    const int64_t col = (int64_t)kvh * a.kv_st_head + 8 * c;
-    const uint8_t *kbase = (const uint8_t *)a.k;
-    const uint8_t *vbase = (const uint8_t *)a.v;
+    const int last_page = (max(kv_end, 1) - 1) >> lbs;     // later table entries are never read
+    const uint8_t *kbase = (const uint8_t *)a.k + (int64_t)kvh * a.kv_st_head * KVB;
+    const uint8_t *vbase = (const uint8_t *)a.v + (int64_t)kvh * a.kv_st_head * KVB;
+    const uint32_t lofs0 = (uint32_t)(lanep * a.kv_st_slot + 8 * c) * KVB;
+    const uint32_t lofs1 = lofs0 + (uint32_t)a.kv_st_slot * KVB;
+    int32_t blk_next[PPT];
     Chunk kr[PPT][2], vr[PPT][2];
 
-    auto load_tile = [&](int tile) {
+    auto fetch_ids = [&](int tile) {
 #pragma unroll
         for (int i = 0; i < PPT; ++i) {
-            const int p = (tid >> 4) + i * (NT / 16);
-            const int j = tile * TN + 2 * p;
-            Chunk k0 = {}, k1 = {}, v0 = {}, v1 = {};
-            if (j < kv_end) {
-                const int64_t blk = btrow[j >> lbs];
-                const int64_t off = blk * a.kv_st_blk + (int64_t)(j & bs_mask) * a.kv_st_slot + col;
-                k0 = *(const Chunk *)(kbase + off * KVB);
-                v0 = *(const Chunk *)(vbase + off * KVB);
-                if (j + 1 < kv_end) {
-                    k1 = *(const Chunk *)(kbase + (off + a.kv_st_slot) * KVB);
-                    v1 = *(const Chunk *)(vbase + (off + a.kv_st_slot) * KVB);
-                }
+            const int jb = tile * TN + 8 * wv + i * (NT / 8);
+            blk_next[i] = sload(btrow + min(jb >> lbs, last_page));
+        }
+    };
+
+    auto load_tile = [&](int tile) {           // page ids of `tile` are in blk_next
+        const bool full = (tile + 1) * TN <= kv_end;
+#pragma unroll
+        for (int i = 0; i < PPT; ++i) {
+            const int jb = tile * TN + 8 * wv + i * (NT / 8);
+            const int64_t pofs =
+                ((int64_t)blk_next[i] * a.kv_st_blk + (int64_t)(jb & bs_mask) * a.kv_st_slot) * KVB;
+            const uint8_t *pk = kbase + pofs;
+            const uint8_t *pv = vbase + pofs;
+            Chunk k0 = *(const Chunk *)(pk + lofs0);
+            Chunk k1 = *(const Chunk *)(pk + lofs1);
+            Chunk v0 = *(const Chunk *)(pv + lofs0);
+            Chunk v1 = *(const Chunk *)(pv + lofs1);
+            if (!full) {
+                // keys at or past kv_end were read from a clamped (allocated)
+                // page; they must contribute nothing
+                const int j0 = jb + lanep;
+                if (j0 >= kv_end) { k0 = Chunk{}; v0 = Chunk{}; }
+                if (j0 + 1 >= kv_end) { k1 = Chunk{}; v1 = Chunk{}; }
             }
             kr[i][0] = k0; kr[i][1] = k1;
             vr[i][0] = v0; vr[i][1] = v1;
         }
     };
 
-    auto store_tile = [&]() {
+    auto store_tile = [&](uint8_t *sK, uint8_t *sV) {
 #pragma unroll
         for (int i = 0; i < PPT; ++i) {
             const int p = (tid >> 4) + i * (NT / 16);
@@ -252,21 +282,22 @@ void attn_fwd_kernel(const AttnArgs a) {
                 k0 = kr[i][0]; k1 = kr[i][1];
                 v0 = vr[i][0]; v1 = vr[i][1];
             }
-            *(u32x4 *)(ldsK + j0 * 256 + ((c ^ swz_k(j0)) << 4)) = k0;
-            *(u32x4 *)(ldsK + j1 * 256 + ((c ^ swz_k(j1)) << 4)) = k1;
-            // V^T[d][j0..j1] as one dword per d
+            *(u32x4 *)(sK + j0 * 256 + ((c ^ swz_k(j0)) << 4)) = k0;
+            *(u32x4 *)(sK + j1 * 256 + ((c ^ swz_k(j1)) << 4)) = k1;
+            // V^T[d][j0..j1] as one dword per d: low halves (even d) and high
+            // halves (odd d) of the two keys' dwords
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const uint32_t even = (v0[e] & 0xffffu) | (v1[e] << 16);          // d = 8c + 2e
-                const uint32_t odd = (v0[e] >> 16) | (v1[e] & 0xffff0000u);       // d = 8c + 2e + 1
+                const uint32_t even = __builtin_amdgcn_perm(v1[e], v0[e], 0x05040100u);
+                const uint32_t odd = __builtin_amdgcn_perm(v1[e], v0[e], 0x07060302u);
                 const int d0 = 8 * c + 2 * e, d1 = d0 + 1;
-                *(uint32_t *)(ldsV + d0 * VROW + (((p >> 2) ^ swz_v<VG>(d0)) << 4) + ((p & 3) << 2)) = even;
-                *(uint32_t *)(ldsV + d1 * VROW + (((p >> 2) ^ swz_v<VG>(d1)) << 4) + ((p & 3) << 2)) = odd;
+                *(uint32_t *)(sV + d0 * VROW + (((p >> 2) ^ swz_v<VG>(d0)) << 4) + ((p & 3) << 2)) = even;
+                *(uint32_t *)(sV + d1 * VROW + (((p >> 2) ^ swz_v<VG>(d1)) << 4) + ((p & 3) << 2)) = odd;
             }
         }
     };
 
-    // ---------------------------------------------------------------- main loop
+    // ---------------------------------------------------------------- compute
     const float c2 = a.scale_log2 * (FP8KV ? *a.k_scale : 1.0f);   // score -> log2 units
     f32x16 o[4];
 #pragma unroll
@@ -275,32 +306,22 @@ void attn_fwd_kernel(const AttnArgs a) {
     float m = neg_inf();        // running max (log2 units, this row)
     float l = 0.0f;             // running sum over this lane half's keys
 
-    if (t_begin < t_end)
-        load_tile(t_begin);
-    for (int tile = t_begin; tile < t_end; ++tile) {
-        __syncthreads();        // previous tile fully consumed
-        store_tile();
-        __syncthreads();        // tile visible to every wave
-        if (tile + 1 < t_end)
-            load_tile(tile + 1);
-        if (!wave_on)
-            continue;
-
+    auto compute_tile = [&](int tile, const uint8_t *sK, const uint8_t *sV) {
         // S^T (keys x rows) for each 32-key block
         f32x16 sacc[NKB];
 #pragma unroll
-        for (int b = 0; b < NKB; ++b) {
+        for (int b = 0; b < NKB; ++b)
             sacc[b] = f32x16{};
-            const uint8_t *krow = ldsK + (32 * b + swap23(lc)) * 256;
 #pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
+        for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+            for (int b = 0; b < NKB; ++b) {
+                const uint8_t *krow = sK + (32 * b + swap23(lc)) * 256;
                 const u32x4 kf = *(const u32x4 *)(krow + (((2 * ks + hl) ^ (lane & 15)) << 4));
                 sacc[b] = mfma32<F16>(kf, qf[ks], sacc[b]);
             }
-        }
 
         // mask (boundary / diagonal tiles only) and row max
-        float mx = neg_inf();
         if (tile >= n_full) {
             const int j0 = tile * TN + 8 * hl;
 #pragma unroll
@@ -312,6 +333,7 @@ void attn_fwd_kernel(const AttnArgs a) {
                         sacc[b][q] = neg_inf();
                 }
         }
+        float mx = neg_inf();
 #pragma unroll
         for (int b = 0; b < NKB; ++b)
 #pragma unroll
@@ -336,16 +358,16 @@ void attn_fwd_kernel(const AttnArgs a) {
                 o[x] *= alpha;
         }
         const float m_use = (m == neg_inf()) ? 0.0f : m;    // fully masked so far: weights 0
-        float rs = 0.0f;
+        float rs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int b = 0; b < NKB; ++b)
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
                 const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[b][q], c2, -m_use));
                 sacc[b][q] = p;
-                rs += p;
+                rs[q & 3] += p;
             }
-        l += rs;
+        l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
 
         // P (16-bit) as the B operand of O^T += V^T P^T
         u32x4 pf[NPV];
@@ -360,15 +382,67 @@ void attn_fwd_kernel(const AttnArgs a) {
                                          pack2<F16>(sacc[b][q0 + 6], sacc[b][q0 + 7])};
             }
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            const int d = 32 * x + lc;
-            const uint8_t *vrow = ldsV + d * VROW;
-            const int sw = swz_v<VG>(d);
+        for (int kk = 0; kk < NPV; ++kk)
 #pragma unroll
-            for (int kk = 0; kk < NPV; ++kk) {
-                const u32x4 vf = *(const u32x4 *)(vrow + (((2 * kk + hl) ^ sw) << 4));
+            for (int x = 0; x < 4; ++x) {
+                const int d = 32 * x + lc;
+                const u32x4 vf =
+                    *(const u32x4 *)(sV + d * VROW + (((2 * kk + hl) ^ swz_v<VG>(d)) << 4));
                 o[x] = mfma32<F16>(vf, pf[kk], o[x]);
             }
+    };
+
+    // ---------------------------------------------------------------- main loop
+    if constexpr (DB) {
+        // Two LDS buffers: compute(tile) reads one while the other receives
+        // tile + 1; one barrier per tile.
+        uint8_t *const sK1 = lds + STAGE;
+        uint8_t *const sV1 = lds + STAGE + TN * 256;
+        if (t_begin < t_end) {
+            fetch_ids(t_begin);
+            load_tile(t_begin);
+            if (t_begin + 1 < t_end)
+                fetch_ids(t_begin + 1);
+            store_tile(ldsK, ldsV);
+            __syncthreads();
+            if (t_begin + 1 < t_end) {
+                load_tile(t_begin + 1);
+                if (t_begin + 2 < t_end)
+                    fetch_ids(t_begin + 2);
+            }
+        }
+        for (int tile = t_begin; tile < t_end; ++tile) {
+            const bool odd = ((tile - t_begin) & 1) != 0;
+            if (wave_on)
+                compute_tile(tile, odd ? sK1 : ldsK, odd ? sV1 : ldsV);
+            if (tile + 1 < t_end) {
+                store_tile(odd ? ldsK : sK1, odd ? ldsV : sV1);
+                __syncthreads();
+                if (tile + 2 < t_end) {
+                    load_tile(tile + 2);
+                    if (tile + 3 < t_end)
+                        fetch_ids(tile + 3);
+                }
+            }
+        }
+    } else {
+        if (t_begin < t_end) {
+            fetch_ids(t_begin);
+            load_tile(t_begin);
+            if (t_begin + 1 < t_end)
+                fetch_ids(t_begin + 1);
+        }
+        for (int tile = t_begin; tile < t_end; ++tile) {
+            __syncthreads();        // previous tile fully consumed
+            store_tile(ldsK, ldsV);
+            __syncthreads();        // tile visible to every wave
+            if (tile + 1 < t_end) {
+                load_tile(tile + 1);
+                if (tile + 2 < t_end)
+                    fetch_ids(tile + 2);
+            }
+            if (wave_on)
+                compute_tile(tile, ldsK, ldsV);
         }
     }
 
