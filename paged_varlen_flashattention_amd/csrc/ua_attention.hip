@@ -115,14 +115,24 @@ __device__ __forceinline__ int swap23(int j) {
     return (j & ~12) | ((j >> 1) & 4) | ((j << 1) & 8);
 }
 
-// LDS swizzles (16-byte granules, XOR):
-//   K tile [TN][128] of 16-bit: granule g of row j is stored at g ^ swz_k(j),
-//   so the 8 lanes that read rows swap23(0..7) hit 8 distinct bank groups.
-//   V^T tile [128][TN]: granule g of row d is stored at g ^ swz_v(d); readers
-//   (consecutive d) and writers (d = 8c + i, c across lanes) both spread.
+// LDS swizzles (16-byte granules, XOR), K and V tiles both [TN][128] 16-bit:
+//   K: granule g of key row j is stored at g ^ swz_k(j), so the 8 lanes that
+//      read rows swap23(0..7) with one 16-byte read hit 8 distinct bank groups;
+//   V: granule g of key row j is stored at g ^ swz_v(j); a transposing read
+//      group covers 4 consecutive keys x 2 granules, which swz_v spreads over 8
+//      distinct granule positions.
 __device__ __forceinline__ int swz_k(int j) { return swap23(j & 15); }
-template <int VG>
-__device__ __forceinline__ int swz_v(int d) { return (d + (d >> 3)) & (VG - 1); }
+__device__ __forceinline__ int swz_v(int j) { return (j & 3) << 1; }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Transposing 8-byte LDS read (ds_read_b64_tr_b16).  Within each 16-lane
+// group, lane i receives element i%4 of the 8 bytes addressed by lane 4e + i/4,
+// for e = 0..3.
+__device__ __forceinline__ s16x4 ds_read_tr16(const uint8_t *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4 *)(p));
+}
 
 // Two waves per SIMD: the kernel is written to fit 256 VGPRs so that the
 // softmax of one wave overlaps the MFMAs of the other.
@@ -134,14 +144,12 @@ void attn_fwd_kernel(const AttnArgs a) {
     constexpr int NPV = TN / 16;                // 16-key steps per tile (PV MFMA K)
     constexpr int PAIRS = (TN / 2) * 16;        // (key pair, 8-d chunk) units per tile
     constexpr int PPT = PAIRS / NT;             // units per thread
-    constexpr int VROW = TN * 2;                // bytes per V^T row
-    constexpr int VG = TN / 8;                  // 16-byte granules per V^T row
     constexpr int KVB = FP8KV ? 1 : 2;          // bytes per cached element
     static_assert(PPT >= 1 && PAIRS % NT == 0, "tile / thread mismatch");
     using Chunk = typename std::conditional<FP8KV, u32x2, u32x4>::type;
 
     constexpr bool DB = NW > 1;                 // double-buffered LDS (prefill tile)
-    constexpr int STAGE = TN * 256 + HD * VROW; // bytes of one K + V^T stage
+    constexpr int STAGE = 2 * TN * 256;         // bytes of one K + V stage
     __shared__ __attribute__((aligned(16))) uint8_t lds[(DB ? 2 : 1) * STAGE];
     uint8_t *const ldsK = lds;
     uint8_t *const ldsV = lds + TN * 256;
@@ -284,16 +292,8 @@ void attn_fwd_kernel(const AttnArgs a) {
             }
             *(u32x4 *)(sK + j0 * 256 + ((c ^ swz_k(j0)) << 4)) = k0;
             *(u32x4 *)(sK + j1 * 256 + ((c ^ swz_k(j1)) << 4)) = k1;
-            // V^T[d][j0..j1] as one dword per d: low halves (even d) and high
-            // halves (odd d) of the two keys' dwords
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t even = __builtin_amdgcn_perm(v1[e], v0[e], 0x05040100u);
-                const uint32_t odd = __builtin_amdgcn_perm(v1[e], v0[e], 0x07060302u);
-                const int d0 = 8 * c + 2 * e, d1 = d0 + 1;
-                *(uint32_t *)(sV + d0 * VROW + (((p >> 2) ^ swz_v<VG>(d0)) << 4) + ((p & 3) << 2)) = even;
-                *(uint32_t *)(sV + d1 * VROW + (((p >> 2) ^ swz_v<VG>(d1)) << 4) + ((p & 3) << 2)) = odd;
-            }
+            *(u32x4 *)(sV + j0 * 256 + ((c ^ swz_v(j0)) << 4)) = v0;
+            *(u32x4 *)(sV + j1 * 256 + ((c ^ swz_v(j1)) << 4)) = v1;
         }
     };
 
@@ -358,6 +358,7 @@ void attn_fwd_kernel(const AttnArgs a) {
                 o[x] *= alpha;
         }
         const float m_use = (m == neg_inf()) ? 0.0f : m;    // fully masked so far: weights 0
+        // weights and their fp32 row sum (four partial sums for ILP)
         float rs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int b = 0; b < NKB; ++b)
@@ -381,14 +382,24 @@ void attn_fwd_kernel(const AttnArgs a) {
                                          pack2<F16>(sacc[b][q0 + 4], sacc[b][q0 + 5]),
                                          pack2<F16>(sacc[b][q0 + 6], sacc[b][q0 + 7])};
             }
+        // V^T fragment of 16-lane group g = lane/16 (d 32x + 16(g&1) .. +15,
+        // keys 16kk + 8(g>>1) .. +7) by two transposing LDS reads: lane j of the
+        // group points at key +4t + j/4, d +4(j%4) .. +3, and receives
+        // V[key + 4t + e][d + j] for e = 0..3.
+        const int jg = lane & 15;
+        const int vrow0 = 8 * hl + (jg >> 2);                // key within a 16-key step
+        const int vsw = swz_v(vrow0);
 #pragma unroll
         for (int kk = 0; kk < NPV; ++kk)
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
-                const int d = 32 * x + lc;
-                const u32x4 vf =
-                    *(const u32x4 *)(sV + d * VROW + (((2 * kk + hl) ^ swz_v<VG>(d)) << 4));
-                o[x] = mfma32<F16>(vf, pf[kk], o[x]);
+                const int gran = 4 * x + 2 * ((lane >> 4) & 1) + ((jg & 3) >> 1);
+                const uint8_t *va = sV + (16 * kk + vrow0) * 256 + ((gran ^ vsw) << 4) + 8 * (jg & 1);
+                const s16x4 r0 = ds_read_tr16(va);
+                const s16x4 r1 = ds_read_tr16(va + 4 * 256);
+                const u32x2 w0 = __builtin_bit_cast(u32x2, r0);
+                const u32x2 w1 = __builtin_bit_cast(u32x2, r1);
+                o[x] = mfma32<F16>(u32x4{w0[0], w0[1], w1[0], w1[1]}, pf[kk], o[x]);
             }
     };
 
@@ -411,12 +422,12 @@ void attn_fwd_kernel(const AttnArgs a) {
                     fetch_ids(t_begin + 2);
             }
         }
-        for (int tile = t_begin; tile < t_end; ++tile) {
-            const bool odd = ((tile - t_begin) & 1) != 0;
+        // unrolled by two so that each stage's LDS addresses are constants
+        auto step = [&](int tile, uint8_t *cK, uint8_t *cV, uint8_t *nK, uint8_t *nV) {
             if (wave_on)
-                compute_tile(tile, odd ? sK1 : ldsK, odd ? sV1 : ldsV);
+                compute_tile(tile, cK, cV);
             if (tile + 1 < t_end) {
-                store_tile(odd ? ldsK : sK1, odd ? ldsV : sV1);
+                store_tile(nK, nV);
                 __syncthreads();
                 if (tile + 2 < t_end) {
                     load_tile(tile + 2);
@@ -424,6 +435,11 @@ void attn_fwd_kernel(const AttnArgs a) {
                         fetch_ids(tile + 3);
                 }
             }
+        };
+        for (int tile = t_begin; tile < t_end; tile += 2) {
+            step(tile, ldsK, ldsV, sK1, sV1);
+            if (tile + 1 < t_end)
+                step(tile + 1, sK1, sV1, ldsK, ldsV);
         }
     } else {
         if (t_begin < t_end) {
