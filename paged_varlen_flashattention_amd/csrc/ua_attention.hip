@@ -52,6 +52,9 @@ constexpr int HD = kHeadSize;
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kLog2e = 1.44269504088896341f;
 constexpr float kRescaleLog2 = 8.0f;     // lazy-rescale threshold, log2 units
+// s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left at their
+// maxima (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[15:14])
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -126,6 +129,25 @@ __device__ __forceinline__ int swz_v(int j) { return (j & 3) << 1; }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land
+// at lds_row + 16*l (lds_row must be wave-uniform).  Issued as inline asm so
+// the compiler does not guard every later LDS read with a wait for it; the
+// kernel waits (wait_vmem) and synchronises (barrier) before it reads a stage
+// that such loads filled.
+// The global address is a wave-uniform base plus a per-lane 32-bit offset.
+__device__ __forceinline__ void lds_dma16(const uint8_t *base, uint32_t lane_ofs, uint8_t *lds_row) {
+    const uint32_t la = (uint32_t)reinterpret_cast<uintptr_t>(
+        (__attribute__((address_space(3))) uint8_t *)(lds_row));
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(lane_ofs), "s"(base), "s"(la)
+                 : "memory", "m0");
+}
+
+// Wait until every vector-memory load of this wave has completed (including
+// loads that write LDS directly).
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // Transposing 8-byte LDS read (ds_read_b64_tr_b16).  Within each 16-lane
 // group, lane i receives element i%4 of the 8 bytes addressed by lane 4e + i/4,
 // for e = 0..3.
@@ -149,8 +171,12 @@ void attn_fwd_kernel(const AttnArgs a) {
     using Chunk = typename std::conditional<FP8KV, u32x2, u32x4>::type;
 
     constexpr bool DB = NW > 1;                 // double-buffered LDS (prefill tile)
+    constexpr bool DMA = DB && !FP8KV;          // K/V loaded straight into LDS
     constexpr int STAGE = 2 * TN * 256;         // bytes of one K + V stage
-    __shared__ __attribute__((aligned(16))) uint8_t lds[(DB ? 2 : 1) * STAGE];
+    // The two stages are separate objects so that alias analysis can tell an
+    // LDS read of one stage from a direct-to-LDS load into the other.
+    __shared__ __attribute__((aligned(16))) uint8_t lds[STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_b[DB ? STAGE : 16];
     uint8_t *const ldsK = lds;
     uint8_t *const ldsV = lds + TN * 256;
 
@@ -220,6 +246,9 @@ void attn_fwd_kernel(const AttnArgs a) {
         for (int ks = 0; ks < 8; ++ks)
             qf[ks] = u32x4{0, 0, 0, 0};
     }
+    // Q is resident before the key loop starts (a wait the compiler tracks, so
+    // no later wait is spent on these loads)
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
     // ---------------------------------------------------------------- loader
     // Thread unit i covers keys 2p, 2p+1 of the tile, p = tid/16 + i*NT/16,
@@ -404,11 +433,83 @@ void attn_fwd_kernel(const AttnArgs a) {
     };
 
     // ---------------------------------------------------------------- main loop
-    if constexpr (DB) {
+    if constexpr (DMA) {
+        // 16-bit caches, prefill tile: K/V go straight from HBM into LDS
+        // (global_load_lds, 16 bytes per lane), no register staging.  Wave w
+        // fills keys 16w .. 16w+15 of the tile (one page) with four 4-key
+        // instructions per tensor; lane l of an instruction lands at LDS byte
+        // 16*l of those 4 rows, so it fetches the d chunk whose swizzled
+        // position that is.  Two LDS stages: the DMA of tile + 1 runs under
+        // the compute of tile; one barrier per tile.
+        static_assert(TN / NW == 16, "one 16-key chunk per wave");
+        uint8_t *const sK1 = lds_b;
+        uint8_t *const sV1 = lds_b + TN * 256;
+        const int lrow = lane >> 4;                           // row within a 4-key group
+        const uint32_t rofs = (uint32_t)(lrow * a.kv_st_slot * KVB);
+        uint32_t koff[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            koff[i] = rofs + (uint32_t)(((lane & 15) ^ swz_k(4 * i + lrow)) << 4);
+        const uint32_t voff = rofs + (uint32_t)(((lane & 15) ^ swz_v(lrow)) << 4);
+        const int wrow = 16 * wv;                             // this wave's first key in the tile
+        int32_t blk_dma = 0;
+        auto fetch_id = [&](int tile) {
+            blk_dma = sload(btrow + min((tile * TN + wrow) >> lbs, last_page));
+        };
+        auto dma_tile = [&](int tile, uint8_t *sK, uint8_t *sV) {
+            const int j = tile * TN + wrow;
+            const int64_t pofs =
+                ((int64_t)blk_dma * a.kv_st_blk + (int64_t)(j & bs_mask) * a.kv_st_slot) * KVB;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t gofs = pofs + (int64_t)(4 * i) * a.kv_st_slot * KVB;
+                lds_dma16(kbase + gofs, koff[i], sK + (wrow + 4 * i) * 256);
+                lds_dma16(vbase + gofs, voff, sV + (wrow + 4 * i) * 256);
+            }
+        };
+        // keys at or past kv_end came from a clamped (allocated) page: zero
+        // their V rows so that weight 0 times whatever was there stays 0
+        auto zero_tail = [&](int tile, uint8_t *sV) {
+            if ((tile + 1) * TN > kv_end) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (tile * TN + wrow + 4 * i + lrow >= kv_end)
+                        *(u32x4 *)(sV + (wrow + 4 * i) * 256 + 16 * lane) = u32x4{0, 0, 0, 0};
+            }
+        };
+        if (t_begin < t_end) {
+            fetch_id(t_begin);
+            dma_tile(t_begin, ldsK, ldsV);
+            if (t_begin + 1 < t_end)
+                fetch_id(t_begin + 1);
+            wait_vmem();
+            zero_tail(t_begin, ldsV);
+            __syncthreads();
+        }
+        auto step = [&](int tile, uint8_t *cK, uint8_t *cV, uint8_t *nK, uint8_t *nV) {
+            if (tile + 1 < t_end) {
+                dma_tile(tile + 1, nK, nV);
+                if (tile + 2 < t_end)
+                    fetch_id(tile + 2);
+            }
+            if (wave_on)
+                compute_tile(tile, cK, cV);
+            if (tile + 1 < t_end) {
+                wait_vmem();
+                zero_tail(tile + 1, nV);
+                __syncthreads();
+            }
+        };
+        for (int tile = t_begin; tile < t_end; tile += 2) {
+            step(tile, ldsK, ldsV, sK1, sV1);
+            if (tile + 1 < t_end)
+                step(tile + 1, sK1, sV1, ldsK, ldsV);
+        }
+    } else if constexpr (DB) {
         // Two LDS buffers: compute(tile) reads one while the other receives
         // tile + 1; one barrier per tile.
-        uint8_t *const sK1 = lds + STAGE;
-        uint8_t *const sV1 = lds + STAGE + TN * 256;
+        uint8_t *const sK1 = lds_b;
+        uint8_t *const sV1 = lds_b + TN * 256;
         if (t_begin < t_end) {
             fetch_ids(t_begin);
             load_tile(t_begin);
