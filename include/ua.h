@@ -108,7 +108,8 @@ typedef enum {
  * q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table (when S > 0
  * and T > 0); D == 128; Hq % Hkv == 0 and Hq / Hkv <= 128; bs a power of two
  * in [16, 4096]; W >= ceil(max_seqlen_k / bs); all strides multiples of 8 and
- * positive; q, out, k_cache, v_cache 16-byte aligned; num_splits <= 128.
+ * positive, kv_stride_slot < 2^26; q, out, k_cache, v_cache 16-byte aligned;
+ * num_splits <= 128.
  * S == 0 or T == 0 is a no-op that returns UA_OK.
  */
 typedef struct ua_attn_params {
@@ -141,16 +142,22 @@ typedef struct ua_attn_params {
     float softmax_scale;
 } ua_attn_params;
 
-/* The launch the library chose for a call (filled by ua_plan). */
+/* The launch the library chose for a call (filled by ua_plan).  Two kernels
+ * share the work: the prefill kernel (4 waves x 32 query rows of one kv head
+ * share each 64-key tile) and the decode kernel (every sequence with
+ * q_len * (Hq / Hkv) <= 32 query rows: 4 waves stream disjoint 32-key units
+ * and merge).  When max_seqlen_q * (Hq / Hkv) <= 32 only the decode kernel
+ * runs; otherwise both run and the prefill kernel skips the short sequences. */
 typedef struct ua_plan_info {
-    int32_t block_m;       /* query rows (token x head pairs) per workgroup */
-    int32_t block_q;       /* query tokens per workgroup = block_m / (Hq / Hkv) */
-    int32_t tile_n;        /* keys per KV tile */
-    int32_t num_waves;     /* 64-lane wavefronts per workgroup */
+    int32_t block_m;       /* query rows per prefill workgroup */
+    int32_t block_q;       /* query tokens per prefill workgroup = block_m / (Hq / Hkv) */
+    int32_t tile_n;        /* keys per prefill KV tile */
+    int32_t num_waves;     /* 64-lane wavefronts per workgroup (both kernels) */
     int32_t num_splits;    /* splits actually used (1 = no combine launch) */
-    int32_t reserved;
-    int64_t grid_x;        /* workgroups along (query block slot x kv head) */
-    int64_t grid_y;        /* workgroups along splits */
+    int32_t kernels;       /* bit 0: prefill kernel launched; bit 1: decode kernel launched */
+    int64_t grid_x;        /* prefill workgroups along (query block slot x kv head); 0 if not launched */
+    int64_t grid_y;        /* workgroups along splits (both kernels) */
+    int64_t decode_grid_x; /* decode workgroups along (sequence x kv head); 0 if not launched */
 } ua_plan_info;
 
 /*

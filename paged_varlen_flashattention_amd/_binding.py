@@ -59,11 +59,12 @@ class PlanInfo(ctypes.Structure):
     """Mirror of ua_plan_info."""
     _fields_ = [("block_m", ctypes.c_int32), ("block_q", ctypes.c_int32),
                 ("tile_n", ctypes.c_int32), ("num_waves", ctypes.c_int32),
-                ("num_splits", ctypes.c_int32), ("reserved", ctypes.c_int32),
-                ("grid_x", ctypes.c_int64), ("grid_y", ctypes.c_int64)]
+                ("num_splits", ctypes.c_int32), ("kernels", ctypes.c_int32),
+                ("grid_x", ctypes.c_int64), ("grid_y", ctypes.c_int64),
+                ("decode_grid_x", ctypes.c_int64)]
 
     def as_dict(self) -> dict:
-        return {k: getattr(self, k) for k, _ in self._fields_ if k != "reserved"}
+        return {k: getattr(self, k) for k, _ in self._fields_}
 
 
 _lib: Optional[ctypes.CDLL] = None

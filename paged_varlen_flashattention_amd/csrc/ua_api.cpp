@@ -20,8 +20,6 @@
 
 namespace {
 
-using ua::Tile;
-
 constexpr int kMaxSplits = 128;
 constexpr int kMaxGroup = 128;
 constexpr size_t kAlign = 256;
@@ -92,43 +90,49 @@ ua_status validate(const ua_attn_params *p) {
     for (int64_t st : strides)
         if (st <= 0 || st % 8 != 0)
             return UA_ERR_INVALID_ARG;
+    if (p->kv_stride_slot >= (int64_t(1) << 26))
+        return UA_ERR_UNSUPPORTED;                             // per-lane 32-bit page offsets
     return UA_OK;
 }
 
 struct Plan {
-    Tile tile;
-    ua::TileShape shape;
-    int32_t block_q;
+    bool prefill;          // launch the prefill kernel
+    bool decode;           // launch the decode kernel
+    int32_t block_q;       // tokens per prefill workgroup
     int32_t splits;
-    int64_t qslots;
+    int64_t qslots;        // prefill query-block slots
 };
 
-// Tile choice: the decode tile (1 wave, 32 rows, 32-key tiles) when every
-// query block fits 32 rows; else the prefill tile (4 waves, 128 rows, 64-key
-// tiles).  Split choice for num_splits = 0: enough workgroups for about two
-// rounds over the CUs, each split keeping at least 8 key tiles, within what
-// the workspace holds.
+// Kernel choice: every sequence with q_len * G <= kDecodeRows rows goes to the
+// decode kernel; when max_seqlen_q * G <= kDecodeRows that is every sequence
+// and the prefill kernel is not launched.  Split choice for num_splits = 0:
+// enough workgroups for about two rounds over the CUs (two workgroups of 4
+// waves per CU), each split keeping at least 8 prefill tiles / 8 decode units,
+// within what the workspace holds.
 Plan make_plan(const ua_attn_params *p) {
     Plan pl;
     const int G = p->num_q_heads / p->num_kv_heads;
-    pl.tile = ((int64_t)p->max_seqlen_q * G <= 32) ? Tile::Decode : Tile::Prefill;
-    pl.shape = ua::tile_shape(pl.tile);
-    if (G > pl.shape.block_m) {
-        pl.tile = Tile::Prefill;
-        pl.shape = ua::tile_shape(pl.tile);
-    }
-    pl.block_q = pl.shape.block_m / G;
+    const bool decode_only = (int64_t)p->max_seqlen_q * G <= ua::kDecodeRows;
+    pl.prefill = !decode_only;
+    pl.decode = true;
+    pl.block_q = ua::kPrefillBlockM / G;
     pl.qslots = (int64_t)p->num_tokens / pl.block_q + p->num_seqs;
     int splits = p->num_splits;
     if (splits == 0) {
-        const int64_t blocks_per_seq =
-            ((int64_t)p->max_seqlen_q + pl.block_q - 1) / pl.block_q;
-        int64_t units = std::min<int64_t>(pl.qslots, p->num_seqs * std::max<int64_t>(blocks_per_seq, 1)) *
-                        p->num_kv_heads;
-        const int64_t waves_wanted = 2LL * kNumCUs * 8;        // two rounds at 8 waves per CU
-        const int64_t wg_wanted = waves_wanted / pl.shape.num_waves;
+        int64_t units;
+        int64_t min_keys;
+        if (decode_only) {
+            units = (int64_t)p->num_seqs * p->num_kv_heads;
+            min_keys = 8 * ua::kDecodeUnit;
+        } else {
+            const int64_t blocks_per_seq = ((int64_t)p->max_seqlen_q + pl.block_q - 1) / pl.block_q;
+            units = std::min<int64_t>(pl.qslots, p->num_seqs * std::max<int64_t>(blocks_per_seq, 1)) *
+                    p->num_kv_heads;
+            min_keys = 8 * ua::kPrefillTileN;
+        }
+        const int64_t wg_wanted = 2LL * kNumCUs * 2;
         int64_t want = units > 0 ? (wg_wanted + units - 1) / units : 1;
-        const int64_t max_by_len = std::max<int64_t>(1, p->max_seqlen_k / (8 * pl.shape.tile_n));
+        const int64_t max_by_len = std::max<int64_t>(1, p->max_seqlen_k / min_keys);
         want = std::min<int64_t>({want, max_by_len, (int64_t)kMaxSplits});
         splits = (int)std::max<int64_t>(1, want);
         while (splits > 1 && ua_workspace_size(p->num_tokens, p->num_q_heads, p->head_size, splits) >
@@ -181,13 +185,15 @@ ua_status ua_plan(const ua_attn_params *p, ua_plan_info *plan) {
         if (!p->workspace || !aligned(p->workspace, kAlign) || p->workspace_bytes < need)
             return UA_ERR_WORKSPACE;
     }
-    plan->block_m = pl.shape.block_m;
+    plan->block_m = ua::kPrefillBlockM;
     plan->block_q = pl.block_q;
-    plan->tile_n = pl.shape.tile_n;
-    plan->num_waves = pl.shape.num_waves;
+    plan->tile_n = ua::kPrefillTileN;
+    plan->num_waves = ua::kWaves;
     plan->num_splits = pl.splits;
-    plan->grid_x = pl.qslots * p->num_kv_heads;
+    plan->kernels = (pl.prefill ? 1 : 0) | (pl.decode ? 2 : 0);
+    plan->grid_x = pl.prefill ? pl.qslots * p->num_kv_heads : 0;
     plan->grid_y = pl.splits;
+    plan->decode_grid_x = pl.decode ? (int64_t)p->num_seqs * p->num_kv_heads : 0;
     return UA_OK;
 }
 
@@ -198,7 +204,7 @@ ua_status ua_unified_attention(const ua_attn_params *p, void *stream) {
         return st;
     if (p->num_seqs == 0 || p->num_tokens == 0)
         return UA_OK;
-    if (info.grid_x > 0x7fffffff)
+    if (info.grid_x + info.decode_grid_x > 0x7fffffff)
         return UA_ERR_UNSUPPORTED;
     const Plan pl = make_plan(p);
     const bool split = pl.splits > 1;
@@ -238,12 +244,16 @@ ua_status ua_unified_attention(const ua_attn_params *p, void *stream) {
     a.log2_block_size = ilog2(p->block_size);
     a.num_splits = pl.splits;
     a.num_qslots = (int32_t)pl.qslots;
+    a.short_to_decode = pl.decode ? 1 : 0;
     a.scale_log2 = p->softmax_scale * 1.44269504088896341f;
 
+    a.prefill_wgs = (int32_t)info.grid_x;
+
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const dim3 grid((unsigned)info.grid_x, (unsigned)info.grid_y);
-    if (ua::launch_attention(a, pl.tile, p->q_dtype == UA_FP16, p->kv_dtype == UA_FP8_E4M3FN,
-                             p->causal != 0, split, grid, s) != hipSuccess)
+    const bool f16 = p->q_dtype == UA_FP16, fp8 = p->kv_dtype == UA_FP8_E4M3FN, causal = p->causal != 0;
+    if (ua::launch_attention(a, f16, fp8, causal, split,
+                             dim3((unsigned)(info.grid_x + info.decode_grid_x), (unsigned)info.grid_y),
+                             s) != hipSuccess)
         return UA_ERR_HIP;
     if (split) {
         if (ua::launch_combine(a.o_part, a.lse_part, pl.splits,

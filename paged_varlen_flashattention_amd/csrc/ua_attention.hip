@@ -4,39 +4,47 @@
 // What is computed (page "flashatten takeaways EP2 工程", section "kv cache"):
 // for every packed query row (token, query head) the softmax-weighted sum of
 // the value rows of its sequence's cached keys, softmax(q K^T * scale) V.
-// How it is organised:
-//   * Work tiler.  One workgroup owns BLOCK_Q query tokens x the G query heads
-//     of one kv head (GQA rows, page "vLLM Triton unified attention notes",
-//     section kernel_unified_attention_2d) x one split.  The host sizes the
-//     grid as (T / BLOCK_Q + S) query-block slots without reading device
-//     memory; sequence s owns slots starting at cu[s] / BLOCK_Q + s, and each
-//     workgroup finds its sequence by a binary search over cu_seqlens_q (same
-//     section: find_seq_idx and the slot transform).
-//   * Paged KV gather.  Key j of sequence s is slot j % bs of physical block
-//     block_table[s][j / bs] (same section: four element strides).  A tile of
-//     keys is gathered by the whole workgroup with 16-byte loads (one cache
-//     row = 16 lanes), prefetched into registers one tile ahead, and staged in
-//     LDS: K row-major, V transposed (d-major) so that both MFMA operands read
-//     16 contiguous bytes per lane.  fp8 e4m3fn codes are widened to the q
-//     dtype on the way in (exact), their scales folded into the score scale
-//     and the epilogue.
-//   * Contractions on MFMA 32x32x16 (bf16 or fp16 in, fp32 accumulate).  We
-//     compute S^T = K Q^T, so each lane's accumulator column is one query row:
-//     the row max and sum need one exchange between the two lane halves, the
-//     rescale factor is a per-lane scalar, and the accumulator of S^T is, after
-//     a fixed permutation of the K rows, directly the B operand of
-//     O^T = V^T P^T.
-//   * Online softmax (page "Fused Attention", FA2 tutorial listing, the inner
-//     loop): running max m and sum l in log2 units, alpha = 2^(m_old - m_new)
-//     rescales the accumulator, a single division at the end.  Unlike the
-//     listing, m is only moved when a tile's max exceeds it by 2^8, so most
-//     tiles skip the rescale.  Tiles that
-//     every row of the block sees in full skip the mask (the tutorial's
-//     off-band / on-band split).
-//   * Split-KV (page "flashatten takeaways EP2 工程", section "源代码接口";
-//     page "Fused Attention", section FlashDecoding): each split owns a
-//     contiguous run of key tiles and stores a normalised fp32 partial and its
-//     natural-log log-sum-exp; the combine kernel merges them.
+//
+// One attention kernel (attn_fwd_kernel) runs two workgroup bodies in one
+// launch, sharing one per-tile step:
+//   * prefill_body: one workgroup of 4 waves owns BLOCK_Q = 128 / G
+//     query tokens x the G query heads of one kv head (GQA rows, page "vLLM
+//     Triton unified attention notes", section kernel_unified_attention_2d)
+//     x one split; each wave owns 32 of the 128 rows and all waves share each
+//     64-key tile staged in LDS.  The host sizes the grid as (T / BLOCK_Q + S)
+//     query-block slots without reading device memory; sequence s owns the
+//     slots from cu[s] / BLOCK_Q + s, and each workgroup finds its sequence by
+//     a binary search over cu_seqlens_q (same section: find_seq_idx and the
+//     slot transform).
+//   * decode_body: sequences whose q_len * G rows fit one wave (<= 32).
+//     One workgroup per (sequence, kv head, split); its 4 waves hold the same
+//     rows and stream disjoint 32-key units of the key range independently (K
+//     straight into MFMA registers, V through a wave-private LDS stage), then
+//     merge their four partial softmax states at the end.  No barrier in the
+//     key loop, so each wave keeps its own loads in flight.
+//
+// The per-tile step (attend_tile):
+//   * MFMA 32x32x16 (bf16 or fp16 in, fp32 accumulate) computing S^T = K Q^T,
+//     so each lane's accumulator column is one query row: the row max and sum
+//     need one exchange between the two lane halves, the rescale factor is a
+//     per-lane scalar, and the accumulator of S^T is, after a fixed permutation
+//     of the K rows, directly the B operand of O^T = V^T P^T;
+//   * online softmax (page "Fused Attention", FA2 tutorial listing, the inner
+//     loop): running max m and sum l in log2 units, a single division at the
+//     end.  Unlike the listing, m only moves when a tile's max exceeds it by
+//     2^8, so most tiles skip the accumulator rescale; tiles that every row
+//     sees in full skip the mask (the tutorial's off-band / on-band split).
+//
+// Paged KV gather: key j of sequence s is slot j % bs of physical block
+// block_table[s][j / bs] (page "vLLM Triton unified attention notes", section
+// kernel_unified_attention_2d: four element strides).  fp8 e4m3fn codes are
+// widened to the q dtype on the way into LDS or registers (exact); k_scale is
+// folded into the score scale and v_scale into the epilogue.
+//
+// Split-KV (page "flashatten takeaways EP2 工程", section "源代码接口"; page
+// "Fused Attention", section FlashDecoding): each split owns a contiguous run
+// of key tiles and stores a normalised fp32 partial and its natural-log
+// log-sum-exp; combine_kernel merges them.
 
 #include "ua_internal.h"
 
@@ -55,6 +63,12 @@ constexpr float kRescaleLog2 = 8.0f;     // lazy-rescale threshold, log2 units
 // s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left at their
 // maxima (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[15:14])
 constexpr int kWaitVmcnt0 = 0x0F70;
+// decode merge record per lane: 64 accumulator values, m, l
+constexpr int kDecodeMergeRows = 4 * 16 + 2;
+// LDS of one workgroup: the larger of the prefill stages (2 x (K + V) of 64
+// keys) and the decode merge buffer (4 waves x 66 x 64 floats)
+constexpr int kLdsBytes = (2 * 2 * 64 * 256) > (4 * kDecodeMergeRows * 64 * 4)
+                              ? (2 * 2 * 64 * 256) : (4 * kDecodeMergeRows * 64 * 4);
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -65,6 +79,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
@@ -118,7 +133,7 @@ __device__ __forceinline__ int swap23(int j) {
     return (j & ~12) | ((j >> 1) & 4) | ((j << 1) & 8);
 }
 
-// LDS swizzles (16-byte granules, XOR), K and V tiles both [TN][128] 16-bit:
+// LDS swizzles (16-byte granules, XOR), K and V tiles both [keys][128] 16-bit:
 //   K: granule g of key row j is stored at g ^ swz_k(j), so the 8 lanes that
 //      read rows swap23(0..7) with one 16-byte read hit 8 distinct bank groups;
 //   V: granule g of key row j is stored at g ^ swz_v(j); a transposing read
@@ -127,14 +142,20 @@ __device__ __forceinline__ int swap23(int j) {
 __device__ __forceinline__ int swz_k(int j) { return swap23(j & 15); }
 __device__ __forceinline__ int swz_v(int j) { return (j & 3) << 1; }
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
+// Transposing 8-byte LDS read (ds_read_b64_tr_b16).  Within each 16-lane
+// group, lane i receives element i%4 of the 8 bytes addressed by lane 4e + i/4,
+// for e = 0..3.
+__device__ __forceinline__ s16x4 ds_read_tr16(const uint8_t *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4 *)(p));
+}
 
 // 16 bytes per lane from global memory straight into LDS: lane l's bytes land
-// at lds_row + 16*l (lds_row must be wave-uniform).  Issued as inline asm so
+// at lds_row + 16*l (lds_row must be wave-uniform); the global address is a
+// wave-uniform base plus a per-lane 32-bit offset.  Issued as inline asm so
 // the compiler does not guard every later LDS read with a wait for it; the
 // kernel waits (wait_vmem) and synchronises (barrier) before it reads a stage
 // that such loads filled.
-// The global address is a wave-uniform base plus a per-lane 32-bit offset.
 __device__ __forceinline__ void lds_dma16(const uint8_t *base, uint32_t lane_ofs, uint8_t *lds_row) {
     const uint32_t la = (uint32_t)reinterpret_cast<uintptr_t>(
         (__attribute__((address_space(3))) uint8_t *)(lds_row));
@@ -148,37 +169,200 @@ __device__ __forceinline__ void lds_dma16(const uint8_t *base, uint32_t lane_ofs
 // loads that write LDS directly).
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Transposing 8-byte LDS read (ds_read_b64_tr_b16).  Within each 16-lane
-// group, lane i receives element i%4 of the 8 bytes addressed by lane 4e + i/4,
-// for e = 0..3.
-__device__ __forceinline__ s16x4 ds_read_tr16(const uint8_t *p) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) s16x4 *)(p));
+// ------------------------------------------------------------------ per-tile step
+
+// Online-softmax state of one wave's 32 query rows (row = accumulator column
+// lane % 32; both lane halves hold the same row).
+struct RowState {
+    f32x16 o[4];   // O^T: block x, register r -> d = 32x + 8(r/4) + 4(lane/32) + r%4
+    float m;       // reference max, log2 units (-inf until the row sees a key)
+    float l;       // sum of weights of this lane half's keys, relative to m
+};
+
+__device__ __forceinline__ void init_rows(RowState &st) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+        st.o[x] = f32x16{};
+    st.m = neg_inf();
+    st.l = 0.0f;
 }
 
-// Two waves per SIMD: the kernel is written to fit 256 VGPRs so that the
-// softmax of one wave overlaps the MFMAs of the other.
-template <bool F16, bool FP8KV, bool CAUSAL, bool SPLIT, int NW, int TN>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void attn_fwd_kernel(const AttnArgs a) {
-    constexpr int NT = NW * 64;                 // threads
-    constexpr int NKB = TN / 32;                // 32-key blocks per tile (S^T MFMA M)
-    constexpr int NPV = TN / 16;                // 16-key steps per tile (PV MFMA K)
-    constexpr int PAIRS = (TN / 2) * 16;        // (key pair, 8-d chunk) units per tile
-    constexpr int PPT = PAIRS / NT;             // units per thread
-    constexpr int KVB = FP8KV ? 1 : 2;          // bytes per cached element
-    static_assert(PPT >= 1 && PAIRS % NT == 0, "tile / thread mismatch");
-    using Chunk = typename std::conditional<FP8KV, u32x2, u32x4>::type;
+// One tile of 32*NKB keys against the wave's 32 query rows.
+//   kfrag(b, ks): K A-operand of key block b (MFMA row i = key 32b + swap23(i)),
+//                 d 16ks .. 16ks+15 (8 per lane half);
+//   vfrag(kk, x): V^T A-operand of d block x (row i = d 32x + i) for keys
+//                 16kk .. 16kk+15, slot s of lane half h = key 16kk + 8h + s;
+//   key0:  absolute index of the tile's first key;
+//   masked: apply the per-row visibility limit lim (keys >= lim get weight 0).
+template <bool F16, int NKB, class KF, class VF>
+__device__ __forceinline__ void attend_tile(RowState &st, const u32x4 (&qf)[8], KF kfrag, VF vfrag,
+                                            int key0, bool masked, int lim, float c2, int lane) {
+    constexpr int NPV = 2 * NKB;
+    const int hl = lane >> 5;
+    f32x16 sacc[NKB];
+#pragma unroll
+    for (int b = 0; b < NKB; ++b)
+        sacc[b] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+        for (int b = 0; b < NKB; ++b)
+            sacc[b] = mfma32<F16>(kfrag(b, ks), qf[ks], sacc[b]);
 
-    constexpr bool DB = NW > 1;                 // double-buffered LDS (prefill tile)
-    constexpr bool DMA = DB && !FP8KV;          // K/V loaded straight into LDS
-    constexpr int STAGE = 2 * TN * 256;         // bytes of one K + V stage
-    // The two stages are separate objects so that alias analysis can tell an
-    // LDS read of one stage from a direct-to-LDS load into the other.
-    __shared__ __attribute__((aligned(16))) uint8_t lds[STAGE];
-    __shared__ __attribute__((aligned(16))) uint8_t lds_b[DB ? STAGE : 16];
-    uint8_t *const ldsK = lds;
-    uint8_t *const ldsV = lds + TN * 256;
+    // mask (boundary / diagonal tiles only) and row max
+    if (masked) {
+        const int j0 = key0 + 8 * hl;
+#pragma unroll
+        for (int b = 0; b < NKB; ++b)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int j = j0 + 32 * b + 16 * (q >> 3) + (q & 7);
+                if (j >= lim)
+                    sacc[b][q] = neg_inf();
+            }
+    }
+    float mx = neg_inf();
+#pragma unroll
+    for (int b = 0; b < NKB; ++b)
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+            mx = fmaxf(mx, sacc[b][q]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+
+    // The reference max m only moves when this tile's max exceeds it by more
+    // than kRescaleLog2 (a factor 2^8): weights 2^(s - m) then stay below 256,
+    // and the accumulator and sum are rescaled only on those (rare, after the
+    // first tiles) steps.  The final division by l makes the result
+    // independent of which reference was used.
+    const float tmax = mx * c2;
+    const bool grow = tmax > st.m + kRescaleLog2;           // also true for the first finite max
+    if (__ballot(grow) != 0) {
+        // rows that do not grow keep alpha = 1 (their m may still be -inf)
+        const float alpha = grow ? __builtin_amdgcn_exp2f(st.m - tmax) : 1.0f;  // 0 if m was -inf
+        st.m = grow ? tmax : st.m;
+        st.l *= alpha;
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+            st.o[x] *= alpha;
+    }
+    const float m_use = (st.m == neg_inf()) ? 0.0f : st.m;  // fully masked so far: weights 0
+    // weights and their fp32 row sum (four partial sums for ILP)
+    float rs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int b = 0; b < NKB; ++b)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[b][q], c2, -m_use));
+            sacc[b][q] = p;
+            rs[q & 3] += p;
+        }
+    st.l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+
+    // P (16-bit) as the B operand of O^T += V^T P^T
+    u32x4 pf[NPV];
+#pragma unroll
+    for (int b = 0; b < NKB; ++b)
+#pragma unroll
+        for (int hsel = 0; hsel < 2; ++hsel) {
+            const int q0 = 8 * hsel;
+            pf[2 * b + hsel] = u32x4{pack2<F16>(sacc[b][q0 + 0], sacc[b][q0 + 1]),
+                                     pack2<F16>(sacc[b][q0 + 2], sacc[b][q0 + 3]),
+                                     pack2<F16>(sacc[b][q0 + 4], sacc[b][q0 + 5]),
+                                     pack2<F16>(sacc[b][q0 + 6], sacc[b][q0 + 7])};
+        }
+#pragma unroll
+    for (int kk = 0; kk < NPV; ++kk)
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+            st.o[x] = mfma32<F16>(vfrag(kk, x), pf[kk], st.o[x]);
+}
+
+// V^T fragment from a row-major [keys][128] LDS V tile with the swz_v layout,
+// by two transposing reads.  Lane j of 16-lane group g = lane/16 points at key
+// 16kk + 8(g>>1) + 4t + j/4 (t = 0, 1), d 32x + 16(g&1) + 4(j%4) .. +3, and
+// receives V[16kk + 8(g>>1) + 4t + e][32x + 16(g&1) + j], e = 0..3.
+__device__ __forceinline__ u32x4 vfrag_lds(const uint8_t *sV, int kk, int x, int lane) {
+    const int jg = lane & 15;
+    const int vrow = 16 * kk + 8 * (lane >> 5) + (jg >> 2);
+    const int gran = 4 * x + 2 * ((lane >> 4) & 1) + ((jg & 3) >> 1);
+    const uint8_t *va = sV + vrow * 256 + ((gran ^ swz_v(vrow)) << 4) + 8 * (jg & 1);
+    const u32x2 w0 = __builtin_bit_cast(u32x2, ds_read_tr16(va));
+    const u32x2 w1 = __builtin_bit_cast(u32x2, ds_read_tr16(va + 4 * 256));
+    return u32x4{w0[0], w0[1], w1[0], w1[1]};
+}
+
+// Row epilogue: normalised output (or split partial) and log-sum-exp of the
+// rows of d blocks [x0, x0 + NX).  o holds the blocks' accumulators, m the
+// row's reference max, l_row its full weight sum.
+template <bool F16, bool SPLIT, int NX>
+__device__ __forceinline__ void write_rows(const AttnArgs &a, const f32x16 (&o)[NX], int x0, float m,
+                                           float l_row, float v_scale, int64_t tok, int head, int split,
+                                           int lane, bool write_lse) {
+    const int hl = lane >> 5;
+    const float inv = l_row > 0.0f ? 1.0f / l_row : 0.0f;
+    const float lse = l_row > 0.0f ? m * kLn2 + __logf(l_row) : neg_inf();
+    const float sc = inv * v_scale;
+    if constexpr (!SPLIT) {
+        uint8_t *op = (uint8_t *)a.out + (tok * a.o_st_tok + (int64_t)head * a.o_st_head) * 2;
+#pragma unroll
+        for (int x = 0; x < NX; ++x)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d = 32 * (x0 + x) + 8 * g + 4 * hl;
+                const u32x2 w = {pack2<F16>(o[x][4 * g] * sc, o[x][4 * g + 1] * sc),
+                                 pack2<F16>(o[x][4 * g + 2] * sc, o[x][4 * g + 3] * sc)};
+                *(u32x2 *)(op + d * 2) = w;
+            }
+        if (write_lse && a.lse_out != nullptr && hl == 0)
+            a.lse_out[tok * a.num_q_heads + head] = lse;
+    } else {
+        const int64_t row = ((int64_t)split * a.num_tokens + tok) * a.num_q_heads + head;
+        float *op = a.o_part + row * HD;
+#pragma unroll
+        for (int x = 0; x < NX; ++x)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d = 32 * (x0 + x) + 8 * g + 4 * hl;
+                *(f32x4 *)(op + d) = f32x4{o[x][4 * g] * sc, o[x][4 * g + 1] * sc,
+                                           o[x][4 * g + 2] * sc, o[x][4 * g + 3] * sc};
+            }
+        if (write_lse && hl == 0)
+            a.lse_part[row] = lse;
+    }
+}
+
+// Q fragments of row (tok, head): B operand of S^T = K Q^T, k-step ks covers
+// d 16ks .. 16ks+15 (8 per lane half).  Zero for rows that do not exist.
+__device__ __forceinline__ void load_q(const AttnArgs &a, u32x4 (&qf)[8], bool row_ok, int64_t tok,
+                                       int head, int lane) {
+    if (row_ok) {
+        const uint8_t *qp = (const uint8_t *)a.q + (tok * a.q_st_tok + (int64_t)head * a.q_st_head) * 2;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+            qf[ks] = *(const u32x4 *)(qp + (16 * ks + 8 * (lane >> 5)) * 2);
+    } else {
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+            qf[ks] = u32x4{0, 0, 0, 0};
+    }
+    // Q is resident before the key loop starts (a wait the compiler tracks, so
+    // no later wait is spent on these loads)
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+}
+
+// ------------------------------------------------------------------ prefill kernel
+
+// Prefill workgroup bx: 4 waves x 32 rows, 64-key tiles in two LDS stages.
+template <bool F16, bool FP8KV, bool CAUSAL, bool SPLIT>
+__device__ __forceinline__ void prefill_body(const AttnArgs &a, int bx, uint8_t *lds) {
+    constexpr int NT = 256, TN = 64;
+    constexpr int NKB = TN / 32;                // 32-key blocks per tile
+    constexpr int KVB = FP8KV ? 1 : 2;          // bytes per cached element
+    constexpr int STAGE = 2 * TN * 256;         // bytes of one K + V stage (16-bit in LDS)
+    uint8_t *const sK0 = lds;
+    uint8_t *const sV0 = lds + TN * 256;
+    uint8_t *const sK1 = lds + STAGE;
+    uint8_t *const sV1 = lds + STAGE + TN * 256;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -187,8 +371,8 @@ void attn_fwd_kernel(const AttnArgs a) {
     const int lc = lane & 31;                   // accumulator column = query row in the wave
 
     // ---------------------------------------------------------------- tiler
-    const int kvh = blockIdx.x % a.num_kv_heads;
-    int slot = blockIdx.x / a.num_kv_heads;
+    const int kvh = bx % a.num_kv_heads;
+    int slot = bx / a.num_kv_heads;
     if (CAUSAL)
         slot = a.num_qslots - 1 - slot;         // late (long) query blocks first
     const int split = blockIdx.y;
@@ -203,6 +387,9 @@ void attn_fwd_kernel(const AttnArgs a) {
     const int s = lo;
     const int cu0 = a.cu_seqlens_q[s];
     const int q_len = a.cu_seqlens_q[s + 1] - cu0;
+    const int G = a.group;
+    if (a.short_to_decode && q_len * G <= kDecodeRows)
+        return;                                 // the decode kernel owns this sequence
     const int tq0 = (slot - (cu0 / a.block_q + s)) * a.block_q;
     if (tq0 >= q_len)
         return;                                 // empty slot (uniform, before any barrier)
@@ -223,7 +410,6 @@ void attn_fwd_kernel(const AttnArgs a) {
     }
 
     // ---------------------------------------------------------------- rows
-    const int G = a.group;
     const int r = wave * 32 + lc;
     const int tq = r / G;
     const int hg = r - tq * G;
@@ -233,217 +419,39 @@ void attn_fwd_kernel(const AttnArgs a) {
     const int head = kvh * G + hg;
     const int lim = !row_ok ? 0 : (CAUSAL ? min(kv_len, ctx + t_loc + 1) : kv_len);
     const bool wave_on = wave * 32 < (tq1 - tq0) * G;
-
-    // Q fragments: B operand of S^T = K Q^T, k-step ks covers d 16*ks .. 16*ks+15.
     u32x4 qf[8];
-    if (row_ok) {
-        const uint8_t *qp = (const uint8_t *)a.q + (tok * a.q_st_tok + (int64_t)head * a.q_st_head) * 2;
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks)
-            qf[ks] = *(const u32x4 *)(qp + (16 * ks + 8 * hl) * 2);
-    } else {
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks)
-            qf[ks] = u32x4{0, 0, 0, 0};
-    }
-    // Q is resident before the key loop starts (a wait the compiler tracks, so
-    // no later wait is spent on these loads)
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    load_q(a, qf, row_ok, tok, head, lane);
 
-    // ---------------------------------------------------------------- loader
-    // Thread unit i covers keys 2p, 2p+1 of the tile, p = tid/16 + i*NT/16,
-    // and the d chunk c = tid%16 (d 8c .. 8c+7).  One load instruction of a
-    // wave covers the 8-key group starting at rbase(i) = 8*wave + i*NT/8; a
-    // page holds at least 16 keys, so the page of every load is wave-uniform:
-    // its id is a scalar load of the block table and the page base is scalar
-    // arithmetic, each lane adding a fixed offset (its key in the group, its d
-    // chunk).  Page ids are fetched one tile ahead of the K/V loads that use
-    // them, so no K/V load waits on a block-table load.
-    const int c = tid & 15;
+    // ---------------------------------------------------------------- paging
     const int wv = __builtin_amdgcn_readfirstlane(wave);
-    const int lanep = 2 * ((tid >> 4) & 3);
     const int32_t *btrow = a.block_table + (int64_t)s * a.bt_stride;
     const int lbs = a.log2_block_size;
     const int bs_mask = (1 << lbs) - 1;
     const int last_page = (max(kv_end, 1) - 1) >> lbs;     // later table entries are never read
     const uint8_t *kbase = (const uint8_t *)a.k + (int64_t)kvh * a.kv_st_head * KVB;
     const uint8_t *vbase = (const uint8_t *)a.v + (int64_t)kvh * a.kv_st_head * KVB;
-    const uint32_t lofs0 = (uint32_t)(lanep * a.kv_st_slot + 8 * c) * KVB;
-    const uint32_t lofs1 = lofs0 + (uint32_t)a.kv_st_slot * KVB;
-    int32_t blk_next[PPT];
-    Chunk kr[PPT][2], vr[PPT][2];
 
-    auto fetch_ids = [&](int tile) {
-#pragma unroll
-        for (int i = 0; i < PPT; ++i) {
-            const int jb = tile * TN + 8 * wv + i * (NT / 8);
-            blk_next[i] = sload(btrow + min(jb >> lbs, last_page));
-        }
-    };
-
-    auto load_tile = [&](int tile) {           // page ids of `tile` are in blk_next
-        const bool full = (tile + 1) * TN <= kv_end;
-#pragma unroll
-        for (int i = 0; i < PPT; ++i) {
-            const int jb = tile * TN + 8 * wv + i * (NT / 8);
-            const int64_t pofs =
-                ((int64_t)blk_next[i] * a.kv_st_blk + (int64_t)(jb & bs_mask) * a.kv_st_slot) * KVB;
-            const uint8_t *pk = kbase + pofs;
-            const uint8_t *pv = vbase + pofs;
-            Chunk k0 = *(const Chunk *)(pk + lofs0);
-            Chunk k1 = *(const Chunk *)(pk + lofs1);
-            Chunk v0 = *(const Chunk *)(pv + lofs0);
-            Chunk v1 = *(const Chunk *)(pv + lofs1);
-            if (!full) {
-                // keys at or past kv_end were read from a clamped (allocated)
-                // page; they must contribute nothing
-                const int j0 = jb + lanep;
-                if (j0 >= kv_end) { k0 = Chunk{}; v0 = Chunk{}; }
-                if (j0 + 1 >= kv_end) { k1 = Chunk{}; v1 = Chunk{}; }
-            }
-            kr[i][0] = k0; kr[i][1] = k1;
-            vr[i][0] = v0; vr[i][1] = v1;
-        }
-    };
-
-    auto store_tile = [&](uint8_t *sK, uint8_t *sV) {
-#pragma unroll
-        for (int i = 0; i < PPT; ++i) {
-            const int p = (tid >> 4) + i * (NT / 16);
-            const int j0 = 2 * p, j1 = 2 * p + 1;
-            u32x4 k0, k1, v0, v1;
-            if constexpr (FP8KV) {
-                k0 = widen_fp8<F16>(kr[i][0]); k1 = widen_fp8<F16>(kr[i][1]);
-                v0 = widen_fp8<F16>(vr[i][0]); v1 = widen_fp8<F16>(vr[i][1]);
-            } else {
-                k0 = kr[i][0]; k1 = kr[i][1];
-                v0 = vr[i][0]; v1 = vr[i][1];
-            }
-            *(u32x4 *)(sK + j0 * 256 + ((c ^ swz_k(j0)) << 4)) = k0;
-            *(u32x4 *)(sK + j1 * 256 + ((c ^ swz_k(j1)) << 4)) = k1;
-            *(u32x4 *)(sV + j0 * 256 + ((c ^ swz_v(j0)) << 4)) = v0;
-            *(u32x4 *)(sV + j1 * 256 + ((c ^ swz_v(j1)) << 4)) = v1;
-        }
-    };
-
-    // ---------------------------------------------------------------- compute
     const float c2 = a.scale_log2 * (FP8KV ? *a.k_scale : 1.0f);   // score -> log2 units
-    f32x16 o[4];
-#pragma unroll
-    for (int x = 0; x < 4; ++x)
-        o[x] = f32x16{};
-    float m = neg_inf();        // running max (log2 units, this row)
-    float l = 0.0f;             // running sum over this lane half's keys
-
-    auto compute_tile = [&](int tile, const uint8_t *sK, const uint8_t *sV) {
-        // S^T (keys x rows) for each 32-key block
-        f32x16 sacc[NKB];
-#pragma unroll
-        for (int b = 0; b < NKB; ++b)
-            sacc[b] = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-            for (int b = 0; b < NKB; ++b) {
-                const uint8_t *krow = sK + (32 * b + swap23(lc)) * 256;
-                const u32x4 kf = *(const u32x4 *)(krow + (((2 * ks + hl) ^ (lane & 15)) << 4));
-                sacc[b] = mfma32<F16>(kf, qf[ks], sacc[b]);
-            }
-
-        // mask (boundary / diagonal tiles only) and row max
-        if (tile >= n_full) {
-            const int j0 = tile * TN + 8 * hl;
-#pragma unroll
-            for (int b = 0; b < NKB; ++b)
-#pragma unroll
-                for (int q = 0; q < 16; ++q) {
-                    const int j = j0 + 32 * b + 16 * (q >> 3) + (q & 7);
-                    if (j >= lim)
-                        sacc[b][q] = neg_inf();
-                }
-        }
-        float mx = neg_inf();
-#pragma unroll
-        for (int b = 0; b < NKB; ++b)
-#pragma unroll
-            for (int q = 0; q < 16; ++q)
-                mx = fmaxf(mx, sacc[b][q]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-
-        // The reference max m only moves when this tile's max exceeds it by
-        // more than kRescaleLog2 (a factor 2^8): weights 2^(s - m) then stay
-        // below 256, and the accumulator and sum are rescaled only on those
-        // (rare, after the first tiles) steps.  The final division by l makes
-        // the result independent of which reference was used.
-        const float tmax = mx * c2;
-        const bool grow = tmax > m + kRescaleLog2;          // also true for the first finite max
-        if (__ballot(grow) != 0) {
-            // rows that do not grow keep alpha = 1 (their m may still be -inf)
-            const float alpha = grow ? __builtin_amdgcn_exp2f(m - tmax) : 1.0f;  // 0 if m was -inf
-            m = grow ? tmax : m;
-            l *= alpha;
-#pragma unroll
-            for (int x = 0; x < 4; ++x)
-                o[x] *= alpha;
-        }
-        const float m_use = (m == neg_inf()) ? 0.0f : m;    // fully masked so far: weights 0
-        // weights and their fp32 row sum (four partial sums for ILP)
-        float rs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int b = 0; b < NKB; ++b)
-#pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[b][q], c2, -m_use));
-                sacc[b][q] = p;
-                rs[q & 3] += p;
-            }
-        l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
-
-        // P (16-bit) as the B operand of O^T += V^T P^T
-        u32x4 pf[NPV];
-#pragma unroll
-        for (int b = 0; b < NKB; ++b)
-#pragma unroll
-            for (int hsel = 0; hsel < 2; ++hsel) {
-                const int q0 = 8 * hsel;
-                pf[2 * b + hsel] = u32x4{pack2<F16>(sacc[b][q0 + 0], sacc[b][q0 + 1]),
-                                         pack2<F16>(sacc[b][q0 + 2], sacc[b][q0 + 3]),
-                                         pack2<F16>(sacc[b][q0 + 4], sacc[b][q0 + 5]),
-                                         pack2<F16>(sacc[b][q0 + 6], sacc[b][q0 + 7])};
-            }
-        // V^T fragment of 16-lane group g = lane/16 (d 32x + 16(g&1) .. +15,
-        // keys 16kk + 8(g>>1) .. +7) by two transposing LDS reads: lane j of the
-        // group points at key +4t + j/4, d +4(j%4) .. +3, and receives
-        // V[key + 4t + e][d + j] for e = 0..3.
-        const int jg = lane & 15;
-        const int vrow0 = 8 * hl + (jg >> 2);                // key within a 16-key step
-        const int vsw = swz_v(vrow0);
-#pragma unroll
-        for (int kk = 0; kk < NPV; ++kk)
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const int gran = 4 * x + 2 * ((lane >> 4) & 1) + ((jg & 3) >> 1);
-                const uint8_t *va = sV + (16 * kk + vrow0) * 256 + ((gran ^ vsw) << 4) + 8 * (jg & 1);
-                const s16x4 r0 = ds_read_tr16(va);
-                const s16x4 r1 = ds_read_tr16(va + 4 * 256);
-                const u32x2 w0 = __builtin_bit_cast(u32x2, r0);
-                const u32x2 w1 = __builtin_bit_cast(u32x2, r1);
-                o[x] = mfma32<F16>(u32x4{w0[0], w0[1], w1[0], w1[1]}, pf[kk], o[x]);
-            }
+    RowState st;
+    init_rows(st);
+    auto compute = [&](int tile, const uint8_t *sK, const uint8_t *sV) {
+        const uint8_t *krow = sK + swap23(lc) * 256;
+        auto kf = [&](int b, int ks) {
+            return *(const u32x4 *)(krow + 32 * b * 256 + (((2 * ks + hl) ^ (lane & 15)) << 4));
+        };
+        auto vf = [&](int kk, int x) { return vfrag_lds(sV, kk, x, lane); };
+        attend_tile<F16, NKB>(st, qf, kf, vf, tile * TN, tile >= n_full, lim, c2, lane);
     };
 
-    // ---------------------------------------------------------------- main loop
-    if constexpr (DMA) {
-        // 16-bit caches, prefill tile: K/V go straight from HBM into LDS
-        // (global_load_lds, 16 bytes per lane), no register staging.  Wave w
-        // fills keys 16w .. 16w+15 of the tile (one page) with four 4-key
-        // instructions per tensor; lane l of an instruction lands at LDS byte
-        // 16*l of those 4 rows, so it fetches the d chunk whose swizzled
-        // position that is.  Two LDS stages: the DMA of tile + 1 runs under
-        // the compute of tile; one barrier per tile.
-        static_assert(TN / NW == 16, "one 16-key chunk per wave");
-        uint8_t *const sK1 = lds_b;
-        uint8_t *const sV1 = lds_b + TN * 256;
+    if constexpr (!FP8KV) {
+        // 16-bit caches: K/V go straight from HBM into LDS (global_load_lds,
+        // 16 bytes per lane), no register staging.  Wave w fills keys
+        // 16w .. 16w+15 of the tile (one page: a page holds >= 16 keys) with
+        // four 4-key instructions per tensor; lane l of an instruction lands
+        // at LDS byte 16*l of those 4 rows, so it fetches the d chunk whose
+        // swizzled position that is.  The DMA of tile + 1 runs under the
+        // compute of tile; one barrier per tile.  The page id is a scalar load
+        // fetched a tile ahead.
         const int lrow = lane >> 4;                           // row within a 4-key group
         const uint32_t rofs = (uint32_t)(lrow * a.kv_st_slot * KVB);
         uint32_t koff[4];
@@ -452,14 +460,14 @@ void attn_fwd_kernel(const AttnArgs a) {
             koff[i] = rofs + (uint32_t)(((lane & 15) ^ swz_k(4 * i + lrow)) << 4);
         const uint32_t voff = rofs + (uint32_t)(((lane & 15) ^ swz_v(lrow)) << 4);
         const int wrow = 16 * wv;                             // this wave's first key in the tile
-        int32_t blk_dma = 0;
+        int32_t blk = 0;
         auto fetch_id = [&](int tile) {
-            blk_dma = sload(btrow + min((tile * TN + wrow) >> lbs, last_page));
+            blk = sload(btrow + min((tile * TN + wrow) >> lbs, last_page));
         };
         auto dma_tile = [&](int tile, uint8_t *sK, uint8_t *sV) {
             const int j = tile * TN + wrow;
             const int64_t pofs =
-                ((int64_t)blk_dma * a.kv_st_blk + (int64_t)(j & bs_mask) * a.kv_st_slot) * KVB;
+                ((int64_t)blk * a.kv_st_blk + (int64_t)(j & bs_mask) * a.kv_st_slot) * KVB;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int64_t gofs = pofs + (int64_t)(4 * i) * a.kv_st_slot * KVB;
@@ -479,13 +487,14 @@ void attn_fwd_kernel(const AttnArgs a) {
         };
         if (t_begin < t_end) {
             fetch_id(t_begin);
-            dma_tile(t_begin, ldsK, ldsV);
+            dma_tile(t_begin, sK0, sV0);
             if (t_begin + 1 < t_end)
                 fetch_id(t_begin + 1);
             wait_vmem();
-            zero_tail(t_begin, ldsV);
+            zero_tail(t_begin, sV0);
             __syncthreads();
         }
+        // unrolled by two so that each stage's LDS addresses are constants
         auto step = [&](int tile, uint8_t *cK, uint8_t *cV, uint8_t *nK, uint8_t *nV) {
             if (tile + 1 < t_end) {
                 dma_tile(tile + 1, nK, nV);
@@ -493,7 +502,7 @@ void attn_fwd_kernel(const AttnArgs a) {
                     fetch_id(tile + 2);
             }
             if (wave_on)
-                compute_tile(tile, cK, cV);
+                compute(tile, cK, cV);
             if (tile + 1 < t_end) {
                 wait_vmem();
                 zero_tail(tile + 1, nV);
@@ -501,21 +510,71 @@ void attn_fwd_kernel(const AttnArgs a) {
             }
         };
         for (int tile = t_begin; tile < t_end; tile += 2) {
-            step(tile, ldsK, ldsV, sK1, sV1);
+            step(tile, sK0, sV0, sK1, sV1);
             if (tile + 1 < t_end)
-                step(tile + 1, sK1, sV1, ldsK, ldsV);
+                step(tile + 1, sK1, sV1, sK0, sV0);
         }
-    } else if constexpr (DB) {
-        // Two LDS buffers: compute(tile) reads one while the other receives
-        // tile + 1; one barrier per tile.
-        uint8_t *const sK1 = lds_b;
-        uint8_t *const sV1 = lds_b + TN * 256;
+    } else {
+        // fp8 caches: codes are loaded into registers one tile ahead, widened
+        // to the q dtype and written into the LDS stage.  Thread unit i covers
+        // keys 2p, 2p+1 of the tile, p = tid/16 + 16i, and the d chunk
+        // c = tid%16 (d 8c .. 8c+7); one load instruction of a wave covers an
+        // 8-key group (one page), whose id is a scalar load.
+        constexpr int PPT = (TN / 2) * 16 / NT;
+        const int c = tid & 15;
+        const int lanep = 2 * ((tid >> 4) & 3);
+        const uint32_t lofs0 = (uint32_t)(lanep * a.kv_st_slot + 8 * c) * KVB;
+        const uint32_t lofs1 = lofs0 + (uint32_t)a.kv_st_slot * KVB;
+        int32_t blk_next[PPT];
+        u32x2 kr[PPT][2], vr[PPT][2];
+        auto fetch_ids = [&](int tile) {
+#pragma unroll
+            for (int i = 0; i < PPT; ++i) {
+                const int jb = tile * TN + 8 * wv + i * (NT / 8);
+                blk_next[i] = sload(btrow + min(jb >> lbs, last_page));
+            }
+        };
+        auto load_tile = [&](int tile) {
+            const bool full = (tile + 1) * TN <= kv_end;
+#pragma unroll
+            for (int i = 0; i < PPT; ++i) {
+                const int jb = tile * TN + 8 * wv + i * (NT / 8);
+                const int64_t pofs =
+                    ((int64_t)blk_next[i] * a.kv_st_blk + (int64_t)(jb & bs_mask) * a.kv_st_slot) * KVB;
+                const uint8_t *pk = kbase + pofs;
+                const uint8_t *pv = vbase + pofs;
+                u32x2 k0 = *(const u32x2 *)(pk + lofs0);
+                u32x2 k1 = *(const u32x2 *)(pk + lofs1);
+                u32x2 v0 = *(const u32x2 *)(pv + lofs0);
+                u32x2 v1 = *(const u32x2 *)(pv + lofs1);
+                if (!full) {
+                    // keys at or past kv_end were read from a clamped
+                    // (allocated) page; they must contribute nothing
+                    const int j0 = jb + lanep;
+                    if (j0 >= kv_end) { k0 = u32x2{}; v0 = u32x2{}; }
+                    if (j0 + 1 >= kv_end) { k1 = u32x2{}; v1 = u32x2{}; }
+                }
+                kr[i][0] = k0; kr[i][1] = k1;
+                vr[i][0] = v0; vr[i][1] = v1;
+            }
+        };
+        auto store_tile = [&](uint8_t *sK, uint8_t *sV) {
+#pragma unroll
+            for (int i = 0; i < PPT; ++i) {
+                const int p = (tid >> 4) + i * (NT / 16);
+                const int j0 = 2 * p, j1 = 2 * p + 1;
+                *(u32x4 *)(sK + j0 * 256 + ((c ^ swz_k(j0)) << 4)) = widen_fp8<F16>(kr[i][0]);
+                *(u32x4 *)(sK + j1 * 256 + ((c ^ swz_k(j1)) << 4)) = widen_fp8<F16>(kr[i][1]);
+                *(u32x4 *)(sV + j0 * 256 + ((c ^ swz_v(j0)) << 4)) = widen_fp8<F16>(vr[i][0]);
+                *(u32x4 *)(sV + j1 * 256 + ((c ^ swz_v(j1)) << 4)) = widen_fp8<F16>(vr[i][1]);
+            }
+        };
         if (t_begin < t_end) {
             fetch_ids(t_begin);
             load_tile(t_begin);
             if (t_begin + 1 < t_end)
                 fetch_ids(t_begin + 1);
-            store_tile(ldsK, ldsV);
+            store_tile(sK0, sV0);
             __syncthreads();
             if (t_begin + 1 < t_end) {
                 load_tile(t_begin + 1);
@@ -523,10 +582,10 @@ void attn_fwd_kernel(const AttnArgs a) {
                     fetch_ids(t_begin + 2);
             }
         }
-        // unrolled by two so that each stage's LDS addresses are constants
+        // compute(tile) reads one stage while the other receives tile + 1
         auto step = [&](int tile, uint8_t *cK, uint8_t *cV, uint8_t *nK, uint8_t *nV) {
             if (wave_on)
-                compute_tile(tile, cK, cV);
+                compute(tile, cK, cV);
             if (tile + 1 < t_end) {
                 store_tile(nK, nV);
                 __syncthreads();
@@ -538,135 +597,324 @@ void attn_fwd_kernel(const AttnArgs a) {
             }
         };
         for (int tile = t_begin; tile < t_end; tile += 2) {
-            step(tile, ldsK, ldsV, sK1, sV1);
+            step(tile, sK0, sV0, sK1, sV1);
             if (tile + 1 < t_end)
-                step(tile + 1, sK1, sV1, ldsK, ldsV);
-        }
-    } else {
-        if (t_begin < t_end) {
-            fetch_ids(t_begin);
-            load_tile(t_begin);
-            if (t_begin + 1 < t_end)
-                fetch_ids(t_begin + 1);
-        }
-        for (int tile = t_begin; tile < t_end; ++tile) {
-            __syncthreads();        // previous tile fully consumed
-            store_tile(ldsK, ldsV);
-            __syncthreads();        // tile visible to every wave
-            if (tile + 1 < t_end) {
-                load_tile(tile + 1);
-                if (tile + 2 < t_end)
-                    fetch_ids(tile + 2);
-            }
-            if (wave_on)
-                compute_tile(tile, ldsK, ldsV);
+                step(tile + 1, sK1, sV1, sK0, sV0);
         }
     }
 
     // ---------------------------------------------------------------- epilogue
     if (!wave_on)
         return;
-    const float l_row = l + __shfl_xor(l, 32);
+    const float l_row = st.l + __shfl_xor(st.l, 32);
     if (!row_ok)
         return;
-    const float inv = l_row > 0.0f ? 1.0f / l_row : 0.0f;
-    const float lse = l_row > 0.0f ? m * kLn2 + __logf(l_row) : neg_inf();
-    const float sc = inv * (FP8KV ? *a.v_scale : 1.0f);
-    if constexpr (!SPLIT) {
-        uint8_t *op = (uint8_t *)a.out + (tok * a.o_st_tok + (int64_t)head * a.o_st_head) * 2;
-#pragma unroll
-        for (int x = 0; x < 4; ++x)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int d = 32 * x + 8 * g + 4 * hl;
-                const u32x2 w = {pack2<F16>(o[x][4 * g] * sc, o[x][4 * g + 1] * sc),
-                                 pack2<F16>(o[x][4 * g + 2] * sc, o[x][4 * g + 3] * sc)};
-                *(u32x2 *)(op + d * 2) = w;
-            }
-        if (a.lse_out != nullptr && hl == 0)
-            a.lse_out[tok * a.num_q_heads + head] = lse;
-    } else {
-        const int64_t row = ((int64_t)split * a.num_tokens + tok) * a.num_q_heads + head;
-        float *op = a.o_part + row * HD;
-#pragma unroll
-        for (int x = 0; x < 4; ++x)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int d = 32 * x + 8 * g + 4 * hl;
-                *(f32x4 *)(op + d) = f32x4{o[x][4 * g] * sc, o[x][4 * g + 1] * sc,
-                                           o[x][4 * g + 2] * sc, o[x][4 * g + 3] * sc};
-            }
-        if (hl == 0)
-            a.lse_part[row] = lse;
-    }
+    write_rows<F16, SPLIT, 4>(a, st.o, 0, st.m, l_row, FP8KV ? *a.v_scale : 1.0f, tok, head, split,
+                              lane, true);
 }
 
-// One 32-lane half-wave per row; lane i owns d 4i .. 4i+3.
+// ------------------------------------------------------------------ decode kernel
+
+// Sequences with q_len * G <= 32 rows.  Grid (S * Hkv, splits).  The 4 waves
+// of a workgroup hold the same rows and take the key units u0 + w, u0 + w + 4,
+// ... of the split's range; a unit is 32 keys.  Per unit:
+//   K -> registers in the MFMA A-operand layout (8 loads per 32 keys), one
+//        unit ahead;
+//   V -> registers (row-major 16-byte chunks), one unit ahead, then into the
+//        wave's own LDS stage, read back with transposing reads.
+// The loads of unit u + 4 are in flight while unit u is computed; no barrier
+// until the final merge of the four waves' softmax states.
+template <bool F16, bool FP8KV, bool CAUSAL, bool SPLIT>
+__device__ __forceinline__ void decode_body(const AttnArgs &a, int bx, uint8_t *lds) {
+    constexpr int NW = 4;
+    constexpr int NKB = 1;                      // 32-key blocks per unit
+    constexpr int UK = 32 * NKB;                // keys per unit
+    constexpr int KVB = FP8KV ? 1 : 2;
+    constexpr int VST = UK * 256;               // bytes of a wave's V stage (16-bit in LDS)
+    constexpr int MROWS = kDecodeMergeRows;
+    static_assert(NW * VST <= kLdsBytes && NW * MROWS * 64 * 4 <= kLdsBytes, "LDS budget");
+    using KChunk = typename std::conditional<FP8KV, u32x2, u32x4>::type;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int hl = lane >> 5;
+    const int lc = lane & 31;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+
+    const int s = bx / a.num_kv_heads;
+    const int kvh = bx - s * a.num_kv_heads;
+    const int split = blockIdx.y;
+    const int cu0 = a.cu_seqlens_q[s];
+    const int q_len = a.cu_seqlens_q[s + 1] - cu0;
+    const int G = a.group;
+    if (q_len == 0 || q_len * G > kDecodeRows)
+        return;                                 // empty, or owned by the prefill kernel
+    const int kv_len = a.seqused_k[s];
+    const int ctx = kv_len - q_len;
+    const int kv_end = CAUSAL ? min(kv_len, ctx + q_len) : kv_len;
+    const int full_end = CAUSAL ? min(kv_len, ctx + 1) : kv_len;
+    const int n_units = max(kv_end, 0) / UK + ((max(kv_end, 0) % UK) != 0);
+    const int n_full = max(full_end, 0) / UK;
+    int u_begin = 0, u_end = n_units;
+    if (SPLIT) {
+        const int per = (n_units + a.num_splits - 1) / a.num_splits;
+        u_begin = min(n_units, split * per);
+        u_end = min(n_units, u_begin + per);
+    }
+
+    // rows (the same in every wave)
+    const int tq = lc / G;
+    const int hg = lc - tq * G;
+    const bool row_ok = tq < q_len;
+    const int64_t tok = (int64_t)cu0 + tq;
+    const int head = kvh * G + hg;
+    const int lim = !row_ok ? 0 : (CAUSAL ? min(kv_len, ctx + tq + 1) : kv_len);
+
+    // paging: a unit's keys lie in at most two pages (keys 0-15 and 16-31 of
+    // the unit, a page holding >= 16 keys); their ids are scalar loads fetched
+    // one unit ahead of the K/V loads that use them
+    static_assert(NKB == 1, "one 32-key block per unit");
+    const int32_t *btrow = a.block_table + (int64_t)s * a.bt_stride;
+    const int lbs = a.log2_block_size;
+    const int bs_mask = (1 << lbs) - 1;
+    const int last_page = (max(kv_end, 1) - 1) >> lbs;
+    const uint8_t *kbase = (const uint8_t *)a.k + (int64_t)kvh * a.kv_st_head * KVB;
+    const uint8_t *vbase = (const uint8_t *)a.v + (int64_t)kvh * a.kv_st_head * KVB;
+    int32_t ids[2];
+    auto fetch_ids = [&](int u) {
+        ids[0] = sload(btrow + min((u * UK) >> lbs, last_page));
+        ids[1] = sload(btrow + min((u * UK + 16) >> lbs, last_page));
+    };
+
+    // K: lane loads key swap23(lc) of the unit (its page: keys 0-15 or 16-31),
+    // d 16ks + 8hl .. +7
+    const int kkey = swap23(lc);
+    KChunk kA[NKB][8], kB[NKB][8];
+    auto load_k = [&](int u, KChunk (&kr)[NKB][8]) {
+        const int64_t pofs = (int64_t)((lc & 16) ? ids[1] : ids[0]) * a.kv_st_blk * KVB;
+        const int j = u * UK + kkey;
+        const uint8_t *p = kbase + pofs + ((int64_t)(j & bs_mask) * a.kv_st_slot + 8 * hl) * KVB;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+            kr[0][ks] = *(const KChunk *)(p + 16 * ks * KVB);
+    };
+    // V: 16-bit caches, instruction i covers keys 4i .. 4i+3 of the unit (16
+    // lanes x 16 bytes per key); fp8 caches, keys 8i .. 8i+7 (8 lanes x 16
+    // bytes = 16 codes each).  One page per instruction.
+    constexpr int VKI = FP8KV ? 8 : 4;          // keys per instruction
+    constexpr int VNI = UK / VKI;               // instructions per unit
+    constexpr int VLK = 64 / VKI;               // lanes per key
+    const int vkey = lane / VLK;
+    const int vch = lane % VLK;                 // 16-byte chunk of the cached row
+    const uint32_t vlofs = (uint32_t)(vkey * a.kv_st_slot * KVB + 16 * vch);
+    u32x4 vr[VNI];
+    auto load_v = [&](int u) {
+#pragma unroll
+        for (int i = 0; i < VNI; ++i) {
+            const int jb = u * UK + VKI * i;
+            const int64_t pofs = (int64_t)(VKI * i < 16 ? ids[0] : ids[1]) * a.kv_st_blk * KVB;
+            const uint8_t *p = vbase + pofs + (int64_t)(jb & bs_mask) * a.kv_st_slot * KVB;
+            vr[i] = *(const u32x4 *)(p + vlofs);
+        }
+    };
+    uint8_t *const sV = lds + wv * VST;
+    auto store_v = [&](int u) {
+        const bool full = (u + 1) * UK <= kv_end;
+#pragma unroll
+        for (int i = 0; i < VNI; ++i) {
+            const int row = VKI * i + vkey;
+            u32x4 v = vr[i];
+            if (!full && u * UK + row >= kv_end)
+                v = u32x4{0, 0, 0, 0};          // clamped-page keys weigh 0; zero their values
+            if constexpr (FP8KV) {
+                // 16 codes = d 16vch .. 16vch+15 -> granules 2vch, 2vch+1
+                const int g0 = 2 * vch;
+                *(u32x4 *)(sV + row * 256 + ((g0 ^ swz_v(row)) << 4)) = widen_fp8<F16>(u32x2{v[0], v[1]});
+                *(u32x4 *)(sV + row * 256 + (((g0 + 1) ^ swz_v(row)) << 4)) = widen_fp8<F16>(u32x2{v[2], v[3]});
+            } else {
+                *(u32x4 *)(sV + row * 256 + ((vch ^ swz_v(row)) << 4)) = v;
+            }
+        }
+    };
+
+    RowState st;
+    init_rows(st);
+    u32x4 qf[8];
+    const float c2 = a.scale_log2 * (FP8KV ? *a.k_scale : 1.0f);
+    auto step = [&](int u, KChunk (&kc)[NKB][8], KChunk (&kn)[NKB][8]) {
+        store_v(u);                             // V(u) registers -> this wave's stage
+        if (u + NW < u_end) {                   // ids of u + NW were fetched last step
+            load_k(u + NW, kn);
+            load_v(u + NW);
+            if (u + 2 * NW < u_end)
+                fetch_ids(u + 2 * NW);
+        }
+        auto kf = [&](int b, int ks) {
+            if constexpr (FP8KV)
+                return widen_fp8<F16>(kc[b][ks]);
+            else
+                return kc[b][ks];
+        };
+        auto vf = [&](int kk, int x) { return vfrag_lds(sV, kk, x, lane); };
+        attend_tile<F16, NKB>(st, qf, kf, vf, u * UK, u >= n_full, lim, c2, lane);
+    };
+    // first unit's loads go out before Q's
+    int u = u_begin + wv;
+    if (u < u_end) {
+        fetch_ids(u);
+        load_k(u, kA);
+        load_v(u);
+        if (u + NW < u_end)
+            fetch_ids(u + NW);
+    }
+    load_q(a, qf, row_ok, tok, head, lane);
+    for (; u < u_end; u += 2 * NW) {
+        step(u, kA, kB);
+        if (u + NW < u_end)
+            step(u + NW, kB, kA);
+    }
+
+    // merge the four waves' states: each wave writes (o, m, l) per lane, then
+    // wave w combines d block w of every row and writes it
+    const float l_row = st.l + __shfl_xor(st.l, 32);
+    __syncthreads();                            // every wave is done with its V stage
+    float *mrec = (float *)lds + wv * (MROWS * 64);
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            mrec[(16 * x + i) * 64 + lane] = st.o[x][i];
+    mrec[64 * 64 + lane] = st.m;
+    mrec[65 * 64 + lane] = l_row;
+    __syncthreads();
+    const float *mall = (const float *)lds;
+    float M = neg_inf();
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+        M = fmaxf(M, mall[w * MROWS * 64 + 64 * 64 + lane]);
+    float L = 0.0f;
+    f32x16 ob[1];
+    ob[0] = f32x16{};
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const float mw = mall[w * MROWS * 64 + 64 * 64 + lane];
+        const float sw = (mw == neg_inf()) ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
+        L += sw * mall[w * MROWS * 64 + 65 * 64 + lane];
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            ob[0][i] += sw * mall[w * MROWS * 64 + (16 * wv + i) * 64 + lane];
+    }
+    if (!row_ok)
+        return;
+    write_rows<F16, SPLIT, 1>(a, ob, wv, M, L, FP8KV ? *a.v_scale : 1.0f, tok, head, split, lane,
+                              wv == 0);
+}
+
+// ------------------------------------------------------------------ the kernel
+
+// One launch for both paths: workgroups [0, prefill_wgs) run the prefill body,
+// the rest the decode body, so memory-bound decode work overlaps compute-bound
+// prefill work.  Two waves per SIMD: the bodies fit 256 VGPRs so that the
+// softmax of one wave overlaps the MFMAs of another workgroup's wave.
+template <bool F16, bool FP8KV, bool CAUSAL, bool SPLIT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_kernel(const AttnArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
+    const int bx = blockIdx.x;
+    if (bx < a.prefill_wgs)
+        prefill_body<F16, FP8KV, CAUSAL, SPLIT>(a, bx, lds);
+    else
+        decode_body<F16, FP8KV, CAUSAL, SPLIT>(a, bx - a.prefill_wgs, lds);
+}
+
+// ------------------------------------------------------------------ combine kernel
+
+// One wave per row.  Lane = (split group sg = lane / 16, d chunk c = lane % 16,
+// d 8c .. 8c+7): each lane accumulates the splits p = sg, sg + 4, ..., and the
+// four split groups are summed with two cross-lane exchanges.
 template <bool F16>
 __global__ __launch_bounds__(256) void combine_kernel(const float *o_part, const float *lse_part,
                                                       int32_t P, int64_t rows, int32_t Hq, void *out,
                                                       int64_t o_st_tok, int64_t o_st_head,
                                                       float *lse_out) {
-    const int64_t row = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= rows)
         return;
-    const int i = threadIdx.x & 31;
+    const int lane = threadIdx.x & 63;
+    const int sg = lane >> 4;
+    const int c = lane & 15;
     float L = neg_inf();
-    for (int p = 0; p < P; ++p)
+    for (int p = sg; p < P; p += 4)
         L = fmaxf(L, lse_part[(int64_t)p * rows + row]);
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    L = fmaxf(L, __shfl_xor(L, 16));
+    L = fmaxf(L, __shfl_xor(L, 32));
+    f32x4 a0 = {0.0f, 0.0f, 0.0f, 0.0f}, a1 = a0;
     float wsum = 0.0f;
     if (L != neg_inf()) {
-        for (int p = 0; p < P; ++p) {
+#pragma unroll 2
+        for (int p = sg; p < P; p += 4) {
             const int64_t pr = (int64_t)p * rows + row;
             const float w = __builtin_amdgcn_exp2f((lse_part[pr] - L) * kLog2e);
-            const f32x4 v = *(const f32x4 *)(o_part + pr * HD + 4 * i);
-            acc += w * v;
+            const f32x4 *src = (const f32x4 *)(o_part + pr * HD + 8 * c);
+            a0 += w * src[0];
+            a1 += w * src[1];
             wsum += w;
         }
     }
+#pragma unroll
+    for (int sh = 16; sh <= 32; sh *= 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            a0[e] += __shfl_xor(a0[e], sh);
+            a1[e] += __shfl_xor(a1[e], sh);
+        }
+        wsum += __shfl_xor(wsum, sh);
+    }
+    if (sg != 0)
+        return;
     const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
     const int64_t tok = row / Hq;
     const int64_t head = row - tok * Hq;
-    uint8_t *op = (uint8_t *)out + (tok * o_st_tok + head * o_st_head + 4 * i) * 2;
-    *(u32x2 *)op = u32x2{pack2<F16>(acc[0] * inv, acc[1] * inv), pack2<F16>(acc[2] * inv, acc[3] * inv)};
-    if (lse_out != nullptr && i == 0)
+    uint8_t *op = (uint8_t *)out + (tok * o_st_tok + head * o_st_head + 8 * c) * 2;
+    *(u32x4 *)op = u32x4{pack2<F16>(a0[0] * inv, a0[1] * inv), pack2<F16>(a0[2] * inv, a0[3] * inv),
+                         pack2<F16>(a1[0] * inv, a1[1] * inv), pack2<F16>(a1[2] * inv, a1[3] * inv)};
+    if (lse_out != nullptr && c == 0)
         lse_out[row] = wsum > 0.0f ? L + __logf(wsum) : neg_inf();
 }
 
+// ------------------------------------------------------------------ launchers
+
 template <bool F16, bool FP8KV, bool CAUSAL, bool SPLIT>
-hipError_t launch_tile(const AttnArgs &a, Tile tile, dim3 grid, hipStream_t st) {
-    if (tile == Tile::Prefill)
-        hipLaunchKernelGGL((attn_fwd_kernel<F16, FP8KV, CAUSAL, SPLIT, 4, 64>), grid, dim3(256), 0, st, a);
-    else
-        hipLaunchKernelGGL((attn_fwd_kernel<F16, FP8KV, CAUSAL, SPLIT, 1, 32>), grid, dim3(64), 0, st, a);
+hipError_t launch_kernel(const AttnArgs &a, dim3 grid, hipStream_t st) {
+    hipLaunchKernelGGL((attn_fwd_kernel<F16, FP8KV, CAUSAL, SPLIT>), grid, dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
 template <bool F16, bool FP8KV>
-hipError_t launch_mode(const AttnArgs &a, Tile tile, bool causal, bool split, dim3 grid, hipStream_t st) {
+hipError_t launch_mode(const AttnArgs &a, bool causal, bool split, dim3 grid, hipStream_t st) {
     if (causal)
-        return split ? launch_tile<F16, FP8KV, true, true>(a, tile, grid, st)
-                     : launch_tile<F16, FP8KV, true, false>(a, tile, grid, st);
-    return split ? launch_tile<F16, FP8KV, false, true>(a, tile, grid, st)
-                 : launch_tile<F16, FP8KV, false, false>(a, tile, grid, st);
+        return split ? launch_kernel<F16, FP8KV, true, true>(a, grid, st)
+                     : launch_kernel<F16, FP8KV, true, false>(a, grid, st);
+    return split ? launch_kernel<F16, FP8KV, false, true>(a, grid, st)
+                 : launch_kernel<F16, FP8KV, false, false>(a, grid, st);
 }
 
 }  // namespace
 
-hipError_t launch_attention(const AttnArgs &a, Tile tile, bool q_f16, bool kv_fp8, bool causal,
-                            bool split, dim3 grid, hipStream_t stream) {
+hipError_t launch_attention(const AttnArgs &a, bool q_f16, bool kv_fp8, bool causal, bool split,
+                            dim3 grid, hipStream_t stream) {
     if (q_f16)
-        return kv_fp8 ? launch_mode<true, true>(a, tile, causal, split, grid, stream)
-                      : launch_mode<true, false>(a, tile, causal, split, grid, stream);
-    return kv_fp8 ? launch_mode<false, true>(a, tile, causal, split, grid, stream)
-                  : launch_mode<false, false>(a, tile, causal, split, grid, stream);
+        return kv_fp8 ? launch_mode<true, true>(a, causal, split, grid, stream)
+                      : launch_mode<true, false>(a, causal, split, grid, stream);
+    return kv_fp8 ? launch_mode<false, true>(a, causal, split, grid, stream)
+                  : launch_mode<false, false>(a, causal, split, grid, stream);
 }
 
 hipError_t launch_combine(const float *o_part, const float *lse_part, int32_t num_splits,
                           int64_t rows, int32_t num_q_heads, void *out, bool out_f16,
                           int64_t o_st_tok, int64_t o_st_head, float *lse_out, hipStream_t stream) {
-    const dim3 grid((unsigned)((rows + 7) / 8));
+    const dim3 grid((unsigned)((rows + 3) / 4));
     if (out_f16)
         hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(256), 0, stream, o_part, lse_part,
                            num_splits, rows, num_q_heads, out, o_st_tok, o_st_head, lse_out);

@@ -9,7 +9,11 @@ namespace ua {
 
 constexpr int kHeadSize = 128;
 
-// Arguments of the attention kernel, passed by value.
+// Sequences with at most this many query rows (q_len * G) are handled by the
+// decode kernel when it is launched.
+constexpr int kDecodeRows = 32;
+
+// Arguments of the attention kernels, passed by value.
 struct AttnArgs {
     const void *q;
     const void *k;
@@ -29,33 +33,25 @@ struct AttnArgs {
     int64_t bt_stride;
     int32_t num_seqs, num_tokens, num_q_heads, num_kv_heads;
     int32_t group;                 // Hq / Hkv
-    int32_t block_q;               // query tokens per workgroup
+    int32_t block_q;               // query tokens per prefill workgroup
     int32_t log2_block_size;
     int32_t num_splits;
     int32_t num_qslots;            // T / block_q + S
+    int32_t short_to_decode;       // prefill body skips sequences with q_len * G <= kDecodeRows
+    int32_t prefill_wgs;           // workgroups [0, prefill_wgs) run the prefill body, the rest decode
     float scale_log2;              // softmax_scale * log2(e)
 };
 
-// A compiled tile shape of the attention kernel.
-enum class Tile : int {
-    Prefill = 0,   // 4 waves x 32 query rows, 64-key tiles
-    Decode = 1,    // 1 wave x 32 query rows, 32-key tiles
-};
+constexpr int kPrefillBlockM = 128;   // query rows per prefill workgroup
+constexpr int kPrefillTileN = 64;     // keys per prefill tile
+constexpr int kDecodeUnit = 32;       // keys per decode unit (16-bit caches; 64 for fp8)
+constexpr int kWaves = 4;             // wavefronts per workgroup, both kernels
 
-struct TileShape {
-    int num_waves;
-    int block_m;
-    int tile_n;
-};
-
-inline TileShape tile_shape(Tile t) {
-    return t == Tile::Prefill ? TileShape{4, 128, 64} : TileShape{1, 32, 32};
-}
-
-// Enqueue the attention kernel.  q_f16: q/out are fp16 (else bf16); kv_fp8:
-// the cache holds fp8 e4m3fn codes (else the q dtype).
-hipError_t launch_attention(const AttnArgs &a, Tile tile, bool q_f16, bool kv_fp8, bool causal,
-                            bool split, dim3 grid, hipStream_t stream);
+// Enqueue the attention kernel: grid.x = prefill workgroups (slots x Hkv) +
+// decode workgroups (S x Hkv), grid.y = splits.  q_f16: q/out are fp16 (else
+// bf16); kv_fp8: the cache holds fp8 e4m3fn codes (else the q dtype).
+hipError_t launch_attention(const AttnArgs &a, bool q_f16, bool kv_fp8, bool causal, bool split,
+                            dim3 grid, hipStream_t stream);
 
 // Enqueue the split combine kernel over rows = T * Hq rows.
 hipError_t launch_combine(const float *o_part, const float *lse_part, int32_t num_splits,

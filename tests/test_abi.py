@@ -84,9 +84,10 @@ def plan_status(lib, p):
 def test_valid_plan_decode(lib):
     st, info = plan_status(lib, base_params())
     assert st == 0
-    # decode tile: 32 rows = 8 tokens x G=4 heads; slots = T/8 + S = 32 + 256
-    assert (info.block_m, info.block_q, info.tile_n, info.num_waves) == (32, 8, 32, 1)
-    assert info.grid_x == (256 // 8 + 256) * 8 and info.grid_y == 1
+    # every sequence has q_len * G = 4 <= 32 rows: only the decode kernel, one
+    # workgroup per (sequence, kv head)
+    assert info.kernels == 2 and info.grid_x == 0
+    assert info.decode_grid_x == 256 * 8 and info.grid_y == 1 and info.num_waves == 4
 
 
 def test_valid_plan_prefill(lib):
@@ -97,7 +98,19 @@ def test_valid_plan_prefill(lib):
     st, info = plan_status(lib, p)
     assert st == 0
     assert (info.block_m, info.block_q, info.tile_n, info.num_waves) == (128, 128, 64, 4)
+    assert info.kernels == 3                                   # prefill + decode (short sequences)
     assert info.grid_x == (16384 // 128 + 4) * 32
+    assert info.decode_grid_x == 4 * 32
+
+
+def test_plan_gqa_block_q(lib):
+    # G = 8: 128 rows = 16 tokens per prefill workgroup; q_len 2048 > 32 / 8
+    p = base_params(num_seqs=68, num_tokens=8256, num_q_heads=64, num_kv_heads=8,
+                    max_seqlen_q=2048, max_seqlen_k=16384, block_table_stride=1024,
+                    q_stride_token=64 * 128, o_stride_token=64 * 128)
+    st, info = plan_status(lib, p)
+    assert st == 0 and info.block_q == 16 and info.kernels == 3
+    assert info.grid_x == (8256 // 16 + 68) * 8 and info.decode_grid_x == 68 * 8
 
 
 @pytest.mark.parametrize("field,value,status", [
@@ -137,6 +150,7 @@ def test_valid_plan_prefill(lib):
     ("q_stride_head", 100, B.UA_ERR_INVALID_ARG),      # not a multiple of 8
     ("o_stride_token", 0, B.UA_ERR_INVALID_ARG),
     ("kv_stride_slot", -1024, B.UA_ERR_INVALID_ARG),
+    ("kv_stride_slot", 1 << 26, B.UA_ERR_UNSUPPORTED),
     ("max_seqlen_q", -1, B.UA_ERR_INVALID_ARG),
 ])
 def test_invalid_arguments(lib, field, value, status):
@@ -170,15 +184,20 @@ def test_split_needs_workspace(lib):
 
 
 def test_auto_splits_respect_workspace(lib):
-    st, info = plan_status(lib, base_params(num_splits=0))
+    few = dict(num_seqs=16, num_tokens=16)                           # 128 workgroups unsplit
+    st, info = plan_status(lib, base_params(num_splits=0, **few))
     assert st == 0 and info.num_splits == 1                        # no workspace: no split
-    p = base_params(num_splits=0, workspace=FAKE, workspace_bytes=1 << 40)
+    p = base_params(num_splits=0, workspace=FAKE, workspace_bytes=1 << 40, **few)
     st, info = plan_status(lib, p)
     assert st == 0 and 1 < info.num_splits <= 128
-    small = lib.ua_workspace_size(256, 32, 128, 2)
-    p = base_params(num_splits=0, workspace=FAKE, workspace_bytes=small)
+    small = lib.ua_workspace_size(16, 32, 128, 2)
+    p = base_params(num_splits=0, workspace=FAKE, workspace_bytes=small, **few)
     st, info = plan_status(lib, p)
     assert st == 0 and info.num_splits == 2
+    # plenty of workgroups already: no split even with room for one
+    p = base_params(num_splits=0, workspace=FAKE, workspace_bytes=1 << 40)
+    st, info = plan_status(lib, p)
+    assert st == 0 and info.num_splits == 1
 
 
 def test_workspace_size_edges(lib):
