@@ -165,6 +165,20 @@ __device__ __forceinline__ void lds_dma16(const uint8_t *base, uint32_t lane_ofs
                  : "memory", "m0");
 }
 
+// Combine a value with the one held by the lane 32 positions away (the other
+// half of the wave), on every lane: v_permlane32_swap exchanges the halves of
+// two registers, so with both operands equal to v the two results hold v and
+// its partner in some order, and a commutative op of them is the same on both
+// halves.  No LDS round trip, unlike a shuffle.
+__device__ __forceinline__ float xhalf_max(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Wait until every vector-memory load of this wave has completed (including
 // loads that write LDS directly).
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -227,7 +241,7 @@ __device__ __forceinline__ void attend_tile(RowState &st, const u32x4 (&qf)[8], 
 #pragma unroll
         for (int q = 0; q < 16; ++q)
             mx = fmaxf(mx, sacc[b][q]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = xhalf_max(mx);
 
     // The reference max m only moves when this tile's max exceeds it by more
     // than kRescaleLog2 (a factor 2^8): weights 2^(s - m) then stay below 256,
@@ -246,7 +260,12 @@ __device__ __forceinline__ void attend_tile(RowState &st, const u32x4 (&qf)[8], 
             st.o[x] *= alpha;
     }
     const float m_use = (st.m == neg_inf()) ? 0.0f : st.m;  // fully masked so far: weights 0
-    // weights and their fp32 row sum (four partial sums for ILP)
+    // weights, P (16-bit) as the B operand of O^T += V^T P^T, and the row sum
+    // (four partial sums for ILP).  fp16: the sum is taken over the rounded
+    // fp16 weights the PV product uses (one v_dot2 per pair, fp32
+    // accumulation: half the instructions of fp32 adds); bf16: over the fp32
+    // weights (bf16 rounding of the sum's terms would cost ~2^-9 of the
+    // log-sum-exp).
     float rs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int b = 0; b < NKB; ++b)
@@ -254,22 +273,36 @@ __device__ __forceinline__ void attend_tile(RowState &st, const u32x4 (&qf)[8], 
         for (int q = 0; q < 16; ++q) {
             const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[b][q], c2, -m_use));
             sacc[b][q] = p;
-            rs[q & 3] += p;
+            if constexpr (!F16)
+                rs[q & 3] += p;
         }
-    st.l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
-
-    // P (16-bit) as the B operand of O^T += V^T P^T
     u32x4 pf[NPV];
 #pragma unroll
     for (int b = 0; b < NKB; ++b)
 #pragma unroll
         for (int hsel = 0; hsel < 2; ++hsel) {
             const int q0 = 8 * hsel;
-            pf[2 * b + hsel] = u32x4{pack2<F16>(sacc[b][q0 + 0], sacc[b][q0 + 1]),
-                                     pack2<F16>(sacc[b][q0 + 2], sacc[b][q0 + 3]),
-                                     pack2<F16>(sacc[b][q0 + 4], sacc[b][q0 + 5]),
-                                     pack2<F16>(sacc[b][q0 + 6], sacc[b][q0 + 7])};
+            if constexpr (F16) {
+                // the dot product takes each pair as built, not an element of
+                // pf: the compiler was seen to fold fdot2 over elements of a
+                // bit-cast vector into the first element
+                const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+                f16x2 h[4];
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    h[w] = f16x2{(_Float16)sacc[b][q0 + 2 * w], (_Float16)sacc[b][q0 + 2 * w + 1]};
+                    rs[w] = __builtin_amdgcn_fdot2(h[w], ones, rs[w], false);
+                }
+                pf[2 * b + hsel] = u32x4{__builtin_bit_cast(uint32_t, h[0]), __builtin_bit_cast(uint32_t, h[1]),
+                                         __builtin_bit_cast(uint32_t, h[2]), __builtin_bit_cast(uint32_t, h[3])};
+            } else {
+                pf[2 * b + hsel] = u32x4{pack2<F16>(sacc[b][q0 + 0], sacc[b][q0 + 1]),
+                                         pack2<F16>(sacc[b][q0 + 2], sacc[b][q0 + 3]),
+                                         pack2<F16>(sacc[b][q0 + 4], sacc[b][q0 + 5]),
+                                         pack2<F16>(sacc[b][q0 + 6], sacc[b][q0 + 7])};
+            }
         }
+    st.l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
 #pragma unroll
     for (int kk = 0; kk < NPV; ++kk)
 #pragma unroll
@@ -606,7 +639,7 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, int bx, uint8_t 
     // ---------------------------------------------------------------- epilogue
     if (!wave_on)
         return;
-    const float l_row = st.l + __shfl_xor(st.l, 32);
+    const float l_row = xhalf_sum(st.l);
     if (!row_ok)
         return;
     write_rows<F16, SPLIT, 4>(a, st.o, 0, st.m, l_row, FP8KV ? *a.v_scale : 1.0f, tok, head, split,
@@ -777,7 +810,7 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, int bx, uint8_t *
 
     // merge the four waves' states: each wave writes (o, m, l) per lane, then
     // wave w combines d block w of every row and writes it
-    const float l_row = st.l + __shfl_xor(st.l, 32);
+    const float l_row = xhalf_sum(st.l);
     __syncthreads();                            // every wave is done with its V stage
     float *mrec = (float *)lds + wv * (MROWS * 64);
 #pragma unroll
