@@ -133,14 +133,19 @@ __device__ __forceinline__ int swap23(int j) {
     return (j & ~12) | ((j >> 1) & 4) | ((j << 1) & 8);
 }
 
-// LDS swizzles (16-byte granules, XOR), K and V tiles both [keys][128] 16-bit:
-//   K: granule g of key row j is stored at g ^ swz_k(j), so the 8 lanes that
-//      read rows swap23(0..7) with one 16-byte read hit 8 distinct bank groups;
-//   V: granule g of key row j is stored at g ^ swz_v(j); a transposing read
-//      group covers 4 consecutive keys x 2 granules, which swz_v spreads over 8
-//      distinct granule positions.
+// LDS swizzles (16-byte granules, XOR), K and V tiles both [keys][128] 16-bit.
+// The LDS serves 256 bytes (64 banks) per clock: a 16-byte read is served 16
+// lanes at a time, an 8-byte read 32 lanes at a time, and a pass is free of
+// bank conflicts when its lanes cover the 16 granule positions of a 256-byte
+// row once each.
+//   K: granule g of key row j is stored at g ^ swz_k(j), so the 16 lanes that
+//      read rows swap23(0..15) with one 16-byte read hit 16 distinct positions;
+//   V: granule g of key row j is stored at g ^ swz_v(j); the 32 lanes of a
+//      transposing read cover 4 consecutive keys x 4 consecutive granules
+//      (4x .. 4x+3), and swz_v moves each of the 4 keys to its own group of 4
+//      positions.
 __device__ __forceinline__ int swz_k(int j) { return swap23(j & 15); }
-__device__ __forceinline__ int swz_v(int j) { return (j & 3) << 1; }
+__device__ __forceinline__ int swz_v(int j) { return (j & 3) << 2; }
 
 // Transposing 8-byte LDS read (ds_read_b64_tr_b16).  Within each 16-lane
 // group, lane i receives element i%4 of the 8 bytes addressed by lane 4e + i/4,
