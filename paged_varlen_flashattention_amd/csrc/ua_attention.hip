@@ -222,11 +222,16 @@ __device__ __forceinline__ void attend_tile(RowState &st, const u32x4 (&qf)[8], 
 #pragma unroll
     for (int b = 0; b < NKB; ++b)
         sacc[b] = f32x16{};
+    // the score MFMA chain runs at raised wave priority: when the matrix
+    // pipe frees up, this wave's next MFMA issues ahead of the softmax VALU
+    // work of the other wave on the SIMD
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
         for (int b = 0; b < NKB; ++b)
             sacc[b] = mfma32<F16>(kfrag(b, ks), qf[ks], sacc[b]);
+    __builtin_amdgcn_s_setprio(0);
 
     // mask (boundary / diagonal tiles only) and row max
     if (masked) {
