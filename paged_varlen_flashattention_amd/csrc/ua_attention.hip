@@ -65,10 +65,13 @@ constexpr float kRescaleLog2 = 8.0f;     // lazy-rescale threshold, log2 units
 constexpr int kWaitVmcnt0 = 0x0F70;
 // decode merge record per lane: 64 accumulator values, m, l
 constexpr int kDecodeMergeRows = 4 * 16 + 2;
-// LDS of one workgroup: the larger of the prefill stages (2 x (K + V) of 64
-// keys) and the decode merge buffer (4 waves x 66 x 64 floats)
-constexpr int kLdsBytes = (2 * 2 * 64 * 256) > (4 * kDecodeMergeRows * 64 * 4)
-                              ? (2 * 2 * 64 * 256) : (4 * kDecodeMergeRows * 64 * 4);
+// LDS of one workgroup of nw waves: the larger of the prefill stages (two K
+// and two V tiles of 64 keys) and the decode merge buffer (nw waves x 66 x 64
+// floats)
+constexpr int lds_bytes(int nw) {
+    return (2 * 2 * 64 * 256) > (nw * kDecodeMergeRows * 64 * 4) ? (2 * 2 * 64 * 256)
+                                                                  : (nw * kDecodeMergeRows * 64 * 4);
+}
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -107,16 +110,22 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
     }
 }
 
-// Eight fp8 e4m3fn codes -> eight 16-bit floats of the q dtype (exact: every
-// e4m3fn value is representable in bf16 and in fp16).
+// Eight fp8 e4m3fn codes -> eight 16-bit floats of the q dtype, one
+// conversion per pair (v_cvt_scalef32_pk_{bf16,f16}_fp8 with scale 1: exact,
+// since every e4m3fn value is representable in bf16 and in fp16).
 template <bool F16>
 __device__ __forceinline__ u32x4 widen_fp8(u32x2 v) {
-    f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(v[0], false);
-    f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(v[0], true);
-    f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8(v[1], false);
-    f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8(v[1], true);
-    return u32x4{pack2<F16>(a[0], a[1]), pack2<F16>(b[0], b[1]), pack2<F16>(c[0], c[1]),
-                 pack2<F16>(d[0], d[1])};
+    if constexpr (F16) {
+        return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v[0], 1.0f, false)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v[0], 1.0f, true)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v[1], 1.0f, false)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v[1], 1.0f, true))};
+    } else {
+        return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], 1.0f, false)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], 1.0f, true)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], 1.0f, false)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], 1.0f, true))};
+    }
 }
 
 // A load the compiler must issue as a scalar (SMEM) load: the address is
@@ -206,19 +215,19 @@ __device__ __forceinline__ void init_rows(RowState &st) {
     st.l = 0.0f;
 }
 
-// One tile of 32*NKB keys against the wave's 32 query rows.
+// One tile of 32*NKB keys against the wave's 32 query rows, in three steps
+// (scores, softmax weights, PV product) that attend_tile runs back to back
+// and the ping-pong prefill body runs in different phases.
 //   kfrag(b, ks): K A-operand of key block b (MFMA row i = key 32b + swap23(i)),
 //                 d 16ks .. 16ks+15 (8 per lane half);
 //   vfrag(kk, x): V^T A-operand of d block x (row i = d 32x + i) for keys
 //                 16kk .. 16kk+15, slot s of lane half h = key 16kk + 8h + s;
 //   key0:  absolute index of the tile's first key;
 //   masked: apply the per-row visibility limit lim (keys >= lim get weight 0).
-template <bool F16, int NKB, class KF, class VF>
-__device__ __forceinline__ void attend_tile(RowState &st, const u32x4 (&qf)[8], KF kfrag, VF vfrag,
-                                            int key0, bool masked, int lim, float c2, int lane) {
-    constexpr int NPV = 2 * NKB;
-    const int hl = lane >> 5;
-    f32x16 sacc[NKB];
+
+// S^T of the tile (sacc[b] = key block b).
+template <bool F16, int NKB, class KF>
+__device__ __forceinline__ void tile_scores(f32x16 (&sacc)[NKB], const u32x4 (&qf)[8], KF kfrag) {
 #pragma unroll
     for (int b = 0; b < NKB; ++b)
         sacc[b] = f32x16{};
@@ -232,7 +241,14 @@ __device__ __forceinline__ void attend_tile(RowState &st, const u32x4 (&qf)[8], 
         for (int b = 0; b < NKB; ++b)
             sacc[b] = mfma32<F16>(kfrag(b, ks), qf[ks], sacc[b]);
     __builtin_amdgcn_s_setprio(0);
+}
 
+// Mask, row max, (lazy) rescale of the state, weights and their row sum; the
+// weights leave as the 16-bit B operand pf of O^T += V^T P^T.
+template <bool F16, int NKB>
+__device__ __forceinline__ void tile_softmax(RowState &st, f32x16 (&sacc)[NKB], u32x4 (&pf)[2 * NKB],
+                                             int key0, bool masked, int lim, float c2, int lane) {
+    const int hl = lane >> 5;
     // mask (boundary / diagonal tiles only) and row max
     if (masked) {
         const int j0 = key0 + 8 * hl;
@@ -286,7 +302,6 @@ __device__ __forceinline__ void attend_tile(RowState &st, const u32x4 (&qf)[8], 
             if constexpr (!F16)
                 rs[q & 3] += p;
         }
-    u32x4 pf[NPV];
 #pragma unroll
     for (int b = 0; b < NKB; ++b)
 #pragma unroll
@@ -313,11 +328,26 @@ __device__ __forceinline__ void attend_tile(RowState &st, const u32x4 (&qf)[8], 
             }
         }
     st.l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+}
+
+// O^T += V^T P^T over the tile's 2*NKB 16-key steps.
+template <bool F16, int NKB, class VF>
+__device__ __forceinline__ void tile_pv(RowState &st, const u32x4 (&pf)[2 * NKB], VF vfrag) {
 #pragma unroll
-    for (int kk = 0; kk < NPV; ++kk)
+    for (int kk = 0; kk < 2 * NKB; ++kk)
 #pragma unroll
         for (int x = 0; x < 4; ++x)
             st.o[x] = mfma32<F16>(vfrag(kk, x), pf[kk], st.o[x]);
+}
+
+template <bool F16, int NKB, class KF, class VF>
+__device__ __forceinline__ void attend_tile(RowState &st, const u32x4 (&qf)[8], KF kfrag, VF vfrag,
+                                            int key0, bool masked, int lim, float c2, int lane) {
+    f32x16 sacc[NKB];
+    u32x4 pf[2 * NKB];
+    tile_scores<F16, NKB>(sacc, qf, kfrag);
+    tile_softmax<F16, NKB>(st, sacc, pf, key0, masked, lim, c2, lane);
+    tile_pv<F16, NKB>(st, pf, vfrag);
 }
 
 // V^T fragment from a row-major [keys][128] LDS V tile with the swz_v layout,
@@ -395,6 +425,58 @@ __device__ __forceinline__ void load_q(const AttnArgs &a, u32x4 (&qf)[8], bool r
 
 // ------------------------------------------------------------------ prefill kernel
 
+// Query block of prefill workgroup bx and its key-tile range.  The host sizes
+// the grid as (T / BLOCK_Q + S) query-block slots per kv head without reading
+// device memory; sequence s owns the slots from cu[s] / BLOCK_Q + s, found by
+// a binary search over cu_seqlens_q (page "vLLM Triton unified attention
+// notes", section kernel_unified_attention_2d: find_seq_idx and the slot
+// transform).  False when the slot is empty or the sequence belongs to the
+// decode body (uniform over the workgroup).
+struct PrefillBlock {
+    int kvh, split, s, cu0, q_len, tq0, tq1, kv_len, ctx, kv_end, n_full, t_begin, t_end;
+};
+
+template <bool CAUSAL, bool SPLIT>
+__device__ __forceinline__ bool locate_block(const AttnArgs &a, int bx, int TN, PrefillBlock &B) {
+    B.kvh = bx % a.num_kv_heads;
+    int slot = bx / a.num_kv_heads;
+    if (CAUSAL)
+        slot = a.num_qslots - 1 - slot;         // late (long) query blocks first
+    B.split = blockIdx.y;
+    int lo = 0, hi = a.num_seqs - 1;
+    while (lo < hi) {                           // largest s with cu[s]/BLOCK_Q + s <= slot
+        const int mid = (lo + hi + 1) >> 1;
+        if (a.cu_seqlens_q[mid] / a.block_q + mid <= slot)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    B.s = lo;
+    B.cu0 = a.cu_seqlens_q[lo];
+    B.q_len = a.cu_seqlens_q[lo + 1] - B.cu0;
+    if (a.short_to_decode && B.q_len * a.group <= kDecodeRows)
+        return false;                           // the decode body owns this sequence
+    B.tq0 = (slot - (B.cu0 / a.block_q + lo)) * a.block_q;
+    if (B.tq0 >= B.q_len)
+        return false;                           // empty slot
+    B.tq1 = min(B.q_len, B.tq0 + a.block_q);
+    B.kv_len = a.seqused_k[lo];
+    B.ctx = B.kv_len - B.q_len;                 // keys before the first query
+    // keys seen by some row / by every row of this block
+    B.kv_end = CAUSAL ? min(B.kv_len, B.ctx + B.tq1) : B.kv_len;
+    const int full_end = CAUSAL ? min(B.kv_len, B.ctx + B.tq0 + 1) : B.kv_len;
+    const int n_tiles = max(B.kv_end, 0) / TN + ((max(B.kv_end, 0) % TN) != 0);
+    B.n_full = max(full_end, 0) / TN;
+    B.t_begin = 0;
+    B.t_end = n_tiles;
+    if (SPLIT) {
+        const int per = (n_tiles + a.num_splits - 1) / a.num_splits;
+        B.t_begin = min(n_tiles, B.split * per);
+        B.t_end = min(n_tiles, B.t_begin + per);
+    }
+    return true;
+}
+
 // Prefill workgroup bx: 4 waves x 32 rows, 64-key tiles in two LDS stages.
 template <bool F16, bool FP8KV, bool CAUSAL, bool SPLIT>
 __device__ __forceinline__ void prefill_body(const AttnArgs &a, int bx, uint8_t *lds) {
@@ -414,43 +496,13 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, int bx, uint8_t 
     const int lc = lane & 31;                   // accumulator column = query row in the wave
 
     // ---------------------------------------------------------------- tiler
-    const int kvh = bx % a.num_kv_heads;
-    int slot = bx / a.num_kv_heads;
-    if (CAUSAL)
-        slot = a.num_qslots - 1 - slot;         // late (long) query blocks first
-    const int split = blockIdx.y;
-    int lo = 0, hi = a.num_seqs - 1;
-    while (lo < hi) {                           // largest s with cu[s]/BLOCK_Q + s <= slot
-        const int mid = (lo + hi + 1) >> 1;
-        if (a.cu_seqlens_q[mid] / a.block_q + mid <= slot)
-            lo = mid;
-        else
-            hi = mid - 1;
-    }
-    const int s = lo;
-    const int cu0 = a.cu_seqlens_q[s];
-    const int q_len = a.cu_seqlens_q[s + 1] - cu0;
+    PrefillBlock B;
+    if (!locate_block<CAUSAL, SPLIT>(a, bx, TN, B))
+        return;                                 // uniform, before any barrier
+    const int kvh = B.kvh, split = B.split, s = B.s, cu0 = B.cu0;
+    const int tq0 = B.tq0, tq1 = B.tq1, kv_len = B.kv_len, ctx = B.ctx, kv_end = B.kv_end;
+    const int n_full = B.n_full, t_begin = B.t_begin, t_end = B.t_end;
     const int G = a.group;
-    if (a.short_to_decode && q_len * G <= kDecodeRows)
-        return;                                 // the decode kernel owns this sequence
-    const int tq0 = (slot - (cu0 / a.block_q + s)) * a.block_q;
-    if (tq0 >= q_len)
-        return;                                 // empty slot (uniform, before any barrier)
-    const int tq1 = min(q_len, tq0 + a.block_q);
-    const int kv_len = a.seqused_k[s];
-    const int ctx = kv_len - q_len;             // keys before the first query
-
-    // keys seen by some row / by every row of this block
-    const int kv_end = CAUSAL ? min(kv_len, ctx + tq1) : kv_len;
-    const int full_end = CAUSAL ? min(kv_len, ctx + tq0 + 1) : kv_len;
-    const int n_tiles = max(kv_end, 0) / TN + ((max(kv_end, 0) % TN) != 0);
-    const int n_full = max(full_end, 0) / TN;
-    int t_begin = 0, t_end = n_tiles;
-    if (SPLIT) {
-        const int per = (n_tiles + a.num_splits - 1) / a.num_splits;
-        t_begin = min(n_tiles, split * per);
-        t_end = min(n_tiles, t_begin + per);
-    }
 
     // ---------------------------------------------------------------- rows
     const int r = wave * 32 + lc;
@@ -461,12 +513,12 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, int bx, uint8_t 
     const int64_t tok = (int64_t)cu0 + t_loc;
     const int head = kvh * G + hg;
     const int lim = !row_ok ? 0 : (CAUSAL ? min(kv_len, ctx + t_loc + 1) : kv_len);
-    const bool wave_on = wave * 32 < (tq1 - tq0) * G;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const bool wave_on = wv * 32 < (tq1 - tq0) * G;       // uniform over the wave
     u32x4 qf[8];
     load_q(a, qf, row_ok, tok, head, lane);
 
     // ---------------------------------------------------------------- paging
-    const int wv = __builtin_amdgcn_readfirstlane(wave);
     const int32_t *btrow = a.block_table + (int64_t)s * a.bt_stride;
     const int lbs = a.log2_block_size;
     const int bs_mask = (1 << lbs) - 1;
@@ -539,14 +591,15 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, int bx, uint8_t 
         }
         // unrolled by two so that each stage's LDS addresses are constants
         auto step = [&](int tile, uint8_t *cK, uint8_t *cV, uint8_t *nK, uint8_t *nV) {
-            if (tile + 1 < t_end) {
+            const bool more = tile + 1 < t_end;
+            if (more) {
                 dma_tile(tile + 1, nK, nV);
                 if (tile + 2 < t_end)
                     fetch_id(tile + 2);
             }
             if (wave_on)
                 compute(tile, cK, cV);
-            if (tile + 1 < t_end) {
+            if (more) {
                 wait_vmem();
                 zero_tail(tile + 1, nV);
                 __syncthreads();
@@ -558,18 +611,23 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, int bx, uint8_t 
                 step(tile + 1, sK1, sV1, sK0, sV0);
         }
     } else {
-        // fp8 caches: codes are loaded into registers one tile ahead, widened
-        // to the q dtype and written into the LDS stage.  Thread unit i covers
-        // keys 2p, 2p+1 of the tile, p = tid/16 + 16i, and the d chunk
-        // c = tid%16 (d 8c .. 8c+7); one load instruction of a wave covers an
-        // 8-key group (one page), whose id is a scalar load.
+        // fp8 caches: codes are loaded into registers two tiles ahead (two
+        // register sets, so two tiles of loads are in flight during each
+        // compute), widened to the q dtype and written into the LDS stage.
+        // Thread unit i covers keys 2p, 2p+1 of the tile, p = tid/16 + 16i,
+        // and the d chunk c = tid%16 (d 8c .. 8c+7); one load instruction of a
+        // wave covers an 8-key group (one page), whose id is a scalar load
+        // fetched one tile before the loads that use it.
         constexpr int PPT = (TN / 2) * 16 / NT;
         const int c = tid & 15;
         const int lanep = 2 * ((tid >> 4) & 3);
         const uint32_t lofs0 = (uint32_t)(lanep * a.kv_st_slot + 8 * c) * KVB;
         const uint32_t lofs1 = lofs0 + (uint32_t)a.kv_st_slot * KVB;
+        struct Codes {
+            u32x2 k[PPT][2], v[PPT][2];
+        };
         int32_t blk_next[PPT];
-        u32x2 kr[PPT][2], vr[PPT][2];
+        Codes R0, R1;
         auto fetch_ids = [&](int tile) {
 #pragma unroll
             for (int i = 0; i < PPT; ++i) {
@@ -577,8 +635,7 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, int bx, uint8_t 
                 blk_next[i] = sload(btrow + min(jb >> lbs, last_page));
             }
         };
-        auto load_tile = [&](int tile) {
-            const bool full = (tile + 1) * TN <= kv_end;
+        auto load_tile = [&](int tile, Codes &r) {
 #pragma unroll
             for (int i = 0; i < PPT; ++i) {
                 const int jb = tile * TN + 8 * wv + i * (NT / 8);
@@ -586,63 +643,72 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, int bx, uint8_t 
                     ((int64_t)blk_next[i] * a.kv_st_blk + (int64_t)(jb & bs_mask) * a.kv_st_slot) * KVB;
                 const uint8_t *pk = kbase + pofs;
                 const uint8_t *pv = vbase + pofs;
-                u32x2 k0 = *(const u32x2 *)(pk + lofs0);
-                u32x2 k1 = *(const u32x2 *)(pk + lofs1);
-                u32x2 v0 = *(const u32x2 *)(pv + lofs0);
-                u32x2 v1 = *(const u32x2 *)(pv + lofs1);
-                if (!full) {
-                    // keys at or past kv_end were read from a clamped
-                    // (allocated) page; they must contribute nothing
-                    const int j0 = jb + lanep;
-                    if (j0 >= kv_end) { k0 = u32x2{}; v0 = u32x2{}; }
-                    if (j0 + 1 >= kv_end) { k1 = u32x2{}; v1 = u32x2{}; }
-                }
-                kr[i][0] = k0; kr[i][1] = k1;
-                vr[i][0] = v0; vr[i][1] = v1;
+                r.k[i][0] = *(const u32x2 *)(pk + lofs0);
+                r.k[i][1] = *(const u32x2 *)(pk + lofs1);
+                r.v[i][0] = *(const u32x2 *)(pv + lofs0);
+                r.v[i][1] = *(const u32x2 *)(pv + lofs1);
             }
         };
-        auto store_tile = [&](uint8_t *sK, uint8_t *sV) {
+        // Keys at or past kv_end were read from a clamped (allocated) page
+        // and must contribute nothing: their K and V rows are stored as 0.
+        // (Applied here, when the loaded registers are consumed anyway, and
+        // not at load time, which would make every load wait at once.)
+        auto store_tile = [&](int tile, const Codes &r, uint8_t *sK, uint8_t *sV) {
+            const bool full = (tile + 1) * TN <= kv_end;
 #pragma unroll
             for (int i = 0; i < PPT; ++i) {
                 const int p = (tid >> 4) + i * (NT / 16);
                 const int j0 = 2 * p, j1 = 2 * p + 1;
-                *(u32x4 *)(sK + j0 * 256 + ((c ^ swz_k(j0)) << 4)) = widen_fp8<F16>(kr[i][0]);
-                *(u32x4 *)(sK + j1 * 256 + ((c ^ swz_k(j1)) << 4)) = widen_fp8<F16>(kr[i][1]);
-                *(u32x4 *)(sV + j0 * 256 + ((c ^ swz_v(j0)) << 4)) = widen_fp8<F16>(vr[i][0]);
-                *(u32x4 *)(sV + j1 * 256 + ((c ^ swz_v(j1)) << 4)) = widen_fp8<F16>(vr[i][1]);
+                u32x4 k0 = widen_fp8<F16>(r.k[i][0]), k1 = widen_fp8<F16>(r.k[i][1]);
+                u32x4 v0 = widen_fp8<F16>(r.v[i][0]), v1 = widen_fp8<F16>(r.v[i][1]);
+                if (!full) {
+                    if (tile * TN + j0 >= kv_end) { k0 = u32x4{0, 0, 0, 0}; v0 = u32x4{0, 0, 0, 0}; }
+                    if (tile * TN + j1 >= kv_end) { k1 = u32x4{0, 0, 0, 0}; v1 = u32x4{0, 0, 0, 0}; }
+                }
+                *(u32x4 *)(sK + j0 * 256 + ((c ^ swz_k(j0)) << 4)) = k0;
+                *(u32x4 *)(sK + j1 * 256 + ((c ^ swz_k(j1)) << 4)) = k1;
+                *(u32x4 *)(sV + j0 * 256 + ((c ^ swz_v(j0)) << 4)) = v0;
+                *(u32x4 *)(sV + j1 * 256 + ((c ^ swz_v(j1)) << 4)) = v1;
             }
         };
+        // tile t_begin + k lives in register set R(k % 2) between its load and
+        // its store
         if (t_begin < t_end) {
             fetch_ids(t_begin);
-            load_tile(t_begin);
-            if (t_begin + 1 < t_end)
-                fetch_ids(t_begin + 1);
-            store_tile(sK0, sV0);
-            __syncthreads();
+            load_tile(t_begin, R0);
             if (t_begin + 1 < t_end) {
-                load_tile(t_begin + 1);
-                if (t_begin + 2 < t_end)
-                    fetch_ids(t_begin + 2);
+                fetch_ids(t_begin + 1);
+                load_tile(t_begin + 1, R1);
+            }
+            if (t_begin + 2 < t_end)
+                fetch_ids(t_begin + 2);
+            store_tile(t_begin, R0, sK0, sV0);
+            __syncthreads();
+            if (t_begin + 2 < t_end) {
+                load_tile(t_begin + 2, R0);
+                if (t_begin + 3 < t_end)
+                    fetch_ids(t_begin + 3);
             }
         }
         // compute(tile) reads one stage while the other receives tile + 1
-        auto step = [&](int tile, uint8_t *cK, uint8_t *cV, uint8_t *nK, uint8_t *nV) {
+        // (from set rn, which then receives tile + 3)
+        auto step = [&](int tile, uint8_t *cK, uint8_t *cV, uint8_t *nK, uint8_t *nV, Codes &rn) {
             if (wave_on)
                 compute(tile, cK, cV);
             if (tile + 1 < t_end) {
-                store_tile(nK, nV);
+                store_tile(tile + 1, rn, nK, nV);
                 __syncthreads();
-                if (tile + 2 < t_end) {
-                    load_tile(tile + 2);
-                    if (tile + 3 < t_end)
-                        fetch_ids(tile + 3);
+                if (tile + 3 < t_end) {
+                    load_tile(tile + 3, rn);
+                    if (tile + 4 < t_end)
+                        fetch_ids(tile + 4);
                 }
             }
         };
         for (int tile = t_begin; tile < t_end; tile += 2) {
-            step(tile, sK0, sV0, sK1, sV1);
+            step(tile, sK0, sV0, sK1, sV1, R1);
             if (tile + 1 < t_end)
-                step(tile + 1, sK1, sV1, sK0, sV0);
+                step(tile + 1, sK1, sV1, sK0, sV0, R0);
         }
     }
 
@@ -658,8 +724,8 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, int bx, uint8_t 
 
 // ------------------------------------------------------------------ decode kernel
 
-// Sequences with q_len * G <= 32 rows.  Grid (S * Hkv, splits).  The 4 waves
-// of a workgroup hold the same rows and take the key units u0 + w, u0 + w + 4,
+// Sequences with q_len * G <= 32 rows.  Grid (S * Hkv, splits).  The NW waves
+// of a workgroup hold the same rows and take the key units u0 + w, u0 + w + NW,
 // ... of the split's range; a unit is 32 keys.  Per unit:
 //   K -> registers in the MFMA A-operand layout (8 loads per 32 keys), one
 //        unit ahead;
@@ -667,15 +733,14 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, int bx, uint8_t 
 //        wave's own LDS stage, read back with transposing reads.
 // The loads of unit u + 4 are in flight while unit u is computed; no barrier
 // until the final merge of the four waves' softmax states.
-template <bool F16, bool FP8KV, bool CAUSAL, bool SPLIT>
+template <bool F16, bool FP8KV, bool CAUSAL, bool SPLIT, int NW>
 __device__ __forceinline__ void decode_body(const AttnArgs &a, int bx, uint8_t *lds) {
-    constexpr int NW = 4;
     constexpr int NKB = 1;                      // 32-key blocks per unit
     constexpr int UK = 32 * NKB;                // keys per unit
     constexpr int KVB = FP8KV ? 1 : 2;
     constexpr int VST = UK * 256;               // bytes of a wave's V stage (16-bit in LDS)
     constexpr int MROWS = kDecodeMergeRows;
-    static_assert(NW * VST <= kLdsBytes && NW * MROWS * 64 * 4 <= kLdsBytes, "LDS budget");
+    static_assert(NW * VST <= lds_bytes(NW) && NW * MROWS * 64 * 4 <= lds_bytes(NW), "LDS budget");
     using KChunk = typename std::conditional<FP8KV, u32x2, u32x4>::type;
 
     const int tid = threadIdx.x;
@@ -818,8 +883,8 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, int bx, uint8_t *
             step(u + NW, kB, kA);
     }
 
-    // merge the four waves' states: each wave writes (o, m, l) per lane, then
-    // wave w combines d block w of every row and writes it
+    // merge the waves' states: each wave writes (o, m, l) per lane, then wave
+    // w < 4 combines d block w of every row and writes it
     const float l_row = xhalf_sum(st.l);
     __syncthreads();                            // every wave is done with its V stage
     float *mrec = (float *)lds + wv * (MROWS * 64);
@@ -831,6 +896,8 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, int bx, uint8_t *
     mrec[64 * 64 + lane] = st.m;
     mrec[65 * 64 + lane] = l_row;
     __syncthreads();
+    if (wv >= 4)
+        return;
     const float *mall = (const float *)lds;
     float M = neg_inf();
 #pragma unroll
@@ -858,17 +925,18 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, int bx, uint8_t *
 
 // One launch for both paths: workgroups [0, prefill_wgs) run the prefill body,
 // the rest the decode body, so memory-bound decode work overlaps compute-bound
-// prefill work.  Two waves per SIMD: the bodies fit 256 VGPRs so that the
-// softmax of one wave overlaps the MFMAs of another workgroup's wave.
+// prefill work.  Two workgroups per CU whose waves pair up on each SIMD (wave
+// w of both on SIMD w), so the softmax of one wave overlaps the MFMAs of the
+// other.
 template <bool F16, bool FP8KV, bool CAUSAL, bool SPLIT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(const AttnArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[lds_bytes(kWaves)];
     const int bx = blockIdx.x;
     if (bx < a.prefill_wgs)
         prefill_body<F16, FP8KV, CAUSAL, SPLIT>(a, bx, lds);
     else
-        decode_body<F16, FP8KV, CAUSAL, SPLIT>(a, bx - a.prefill_wgs, lds);
+        decode_body<F16, FP8KV, CAUSAL, SPLIT, kWaves>(a, bx - a.prefill_wgs, lds);
 }
 
 // ------------------------------------------------------------------ combine kernel
@@ -930,7 +998,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *o_part, const
 
 template <bool F16, bool FP8KV, bool CAUSAL, bool SPLIT>
 hipError_t launch_kernel(const AttnArgs &a, dim3 grid, hipStream_t st) {
-    hipLaunchKernelGGL((attn_fwd_kernel<F16, FP8KV, CAUSAL, SPLIT>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<F16, FP8KV, CAUSAL, SPLIT>), grid, dim3(kWaves * 64), 0, st, a);
     return hipGetLastError();
 }
 

@@ -44,8 +44,8 @@ struct AttnArgs {
 
 constexpr int kPrefillBlockM = 128;   // query rows per prefill workgroup
 constexpr int kPrefillTileN = 64;     // keys per prefill tile
-constexpr int kDecodeUnit = 32;       // keys per decode unit (16-bit caches; 64 for fp8)
-constexpr int kWaves = 4;             // wavefronts per workgroup, both kernels
+constexpr int kDecodeUnit = 32;       // keys per decode unit
+constexpr int kWaves = 4;             // wavefronts per workgroup, both bodies
 
 // Enqueue the attention kernel: grid.x = prefill workgroups (slots x Hkv) +
 // decode workgroups (S x Hkv), grid.y = splits.  q_f16: q/out are fp16 (else
