@@ -726,13 +726,14 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, int bx, uint8_t 
 
 // Sequences with q_len * G <= 32 rows.  Grid (S * Hkv, splits).  The NW waves
 // of a workgroup hold the same rows and take the key units u0 + w, u0 + w + NW,
-// ... of the split's range; a unit is 32 keys.  Per unit:
-//   K -> registers in the MFMA A-operand layout (8 loads per 32 keys), one
-//        unit ahead;
-//   V -> registers (row-major 16-byte chunks), one unit ahead, then into the
-//        wave's own LDS stage, read back with transposing reads.
-// The loads of unit u + 4 are in flight while unit u is computed; no barrier
-// until the final merge of the four waves' softmax states.
+// ... of the split's range; a unit is 32 keys.  Per unit, K and V rows are
+// loaded whole (coalesced, one unit ahead) into registers, then written into
+// the wave's own LDS stages, from which the score fragments are read like the
+// prefill body's (K) and the V^T fragments with transposing reads.  (Loading
+// K straight in the MFMA operand layout would make every load instruction
+// touch 32 key rows; whole-row loads stream about 7% faster.)  The loads of
+// unit u + NW are in flight while unit u is computed; no barrier until the
+// final merge of the waves' softmax states.
 template <bool F16, bool FP8KV, bool CAUSAL, bool SPLIT, int NW>
 __device__ __forceinline__ void decode_body(const AttnArgs &a, int bx, uint8_t *lds) {
     constexpr int NKB = 1;                      // 32-key blocks per unit
@@ -740,8 +741,7 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, int bx, uint8_t *
     constexpr int KVB = FP8KV ? 1 : 2;
     constexpr int VST = UK * 256;               // bytes of a wave's V stage (16-bit in LDS)
     constexpr int MROWS = kDecodeMergeRows;
-    static_assert(NW * VST <= lds_bytes(NW) && NW * MROWS * 64 * 4 <= lds_bytes(NW), "LDS budget");
-    using KChunk = typename std::conditional<FP8KV, u32x2, u32x4>::type;
+    static_assert(NW * 2 * VST <= lds_bytes(NW) && NW * MROWS * 64 * 4 <= lds_bytes(NW), "LDS budget");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -795,39 +795,31 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, int bx, uint8_t *
         ids[1] = sload(btrow + min((u * UK + 16) >> lbs, last_page));
     };
 
-    // K: lane loads key swap23(lc) of the unit (its page: keys 0-15 or 16-31),
-    // d 16ks + 8hl .. +7
-    const int kkey = swap23(lc);
-    KChunk kA[NKB][8], kB[NKB][8];
-    auto load_k = [&](int u, KChunk (&kr)[NKB][8]) {
-        const int64_t pofs = (int64_t)((lc & 16) ? ids[1] : ids[0]) * a.kv_st_blk * KVB;
-        const int j = u * UK + kkey;
-        const uint8_t *p = kbase + pofs + ((int64_t)(j & bs_mask) * a.kv_st_slot + 8 * hl) * KVB;
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks)
-            kr[0][ks] = *(const KChunk *)(p + 16 * ks * KVB);
-    };
-    // V: 16-bit caches, instruction i covers keys 4i .. 4i+3 of the unit (16
-    // lanes x 16 bytes per key); fp8 caches, keys 8i .. 8i+7 (8 lanes x 16
-    // bytes = 16 codes each).  One page per instruction.
+    // K and V: 16-bit caches, instruction i covers keys 4i .. 4i+3 of the
+    // unit (16 lanes x 16 bytes per key row); fp8 caches, keys 8i .. 8i+7 (8
+    // lanes x 16 bytes = 16 codes each).  One page per instruction, whole rows
+    // per instruction (coalesced).  Both go through the wave's own LDS stages
+    // (K with the swz_k layout the score fragments are read from, V with swz_v).
     constexpr int VKI = FP8KV ? 8 : 4;          // keys per instruction
     constexpr int VNI = UK / VKI;               // instructions per unit
     constexpr int VLK = 64 / VKI;               // lanes per key
     const int vkey = lane / VLK;
     const int vch = lane % VLK;                 // 16-byte chunk of the cached row
     const uint32_t vlofs = (uint32_t)(vkey * a.kv_st_slot * KVB + 16 * vch);
-    u32x4 vr[VNI];
-    auto load_v = [&](int u) {
+    u32x4 kr[VNI], vr[VNI];
+    auto load_kv = [&](int u) {
 #pragma unroll
         for (int i = 0; i < VNI; ++i) {
             const int jb = u * UK + VKI * i;
-            const int64_t pofs = (int64_t)(VKI * i < 16 ? ids[0] : ids[1]) * a.kv_st_blk * KVB;
-            const uint8_t *p = vbase + pofs + (int64_t)(jb & bs_mask) * a.kv_st_slot * KVB;
-            vr[i] = *(const u32x4 *)(p + vlofs);
+            const int64_t pofs = ((int64_t)(VKI * i < 16 ? ids[0] : ids[1]) * a.kv_st_blk +
+                                  (int64_t)(jb & bs_mask) * a.kv_st_slot) * KVB;
+            kr[i] = *(const u32x4 *)(kbase + pofs + vlofs);
+            vr[i] = *(const u32x4 *)(vbase + pofs + vlofs);
         }
     };
-    uint8_t *const sV = lds + wv * VST;
-    auto store_v = [&](int u) {
+    uint8_t *const sK = lds + wv * (2 * VST);
+    uint8_t *const sV = sK + VST;
+    auto store_kv = [&](int u) {
         const bool full = (u + 1) * UK <= kv_end;
 #pragma unroll
         for (int i = 0; i < VNI; ++i) {
@@ -838,9 +830,12 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, int bx, uint8_t *
             if constexpr (FP8KV) {
                 // 16 codes = d 16vch .. 16vch+15 -> granules 2vch, 2vch+1
                 const int g0 = 2 * vch;
+                *(u32x4 *)(sK + row * 256 + ((g0 ^ swz_k(row)) << 4)) = widen_fp8<F16>(u32x2{kr[i][0], kr[i][1]});
+                *(u32x4 *)(sK + row * 256 + (((g0 + 1) ^ swz_k(row)) << 4)) = widen_fp8<F16>(u32x2{kr[i][2], kr[i][3]});
                 *(u32x4 *)(sV + row * 256 + ((g0 ^ swz_v(row)) << 4)) = widen_fp8<F16>(u32x2{v[0], v[1]});
                 *(u32x4 *)(sV + row * 256 + (((g0 + 1) ^ swz_v(row)) << 4)) = widen_fp8<F16>(u32x2{v[2], v[3]});
             } else {
+                *(u32x4 *)(sK + row * 256 + ((vch ^ swz_k(row)) << 4)) = kr[i];
                 *(u32x4 *)(sV + row * 256 + ((vch ^ swz_v(row)) << 4)) = v;
             }
         }
@@ -850,19 +845,16 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, int bx, uint8_t *
     init_rows(st);
     u32x4 qf[8];
     const float c2 = a.scale_log2 * (FP8KV ? *a.k_scale : 1.0f);
-    auto step = [&](int u, KChunk (&kc)[NKB][8], KChunk (&kn)[NKB][8]) {
-        store_v(u);                             // V(u) registers -> this wave's stage
+    const uint8_t *krow = sK + swap23(lc) * 256;
+    auto step = [&](int u) {
+        store_kv(u);                            // K, V(u) registers -> this wave's stages
         if (u + NW < u_end) {                   // ids of u + NW were fetched last step
-            load_k(u + NW, kn);
-            load_v(u + NW);
+            load_kv(u + NW);
             if (u + 2 * NW < u_end)
                 fetch_ids(u + 2 * NW);
         }
         auto kf = [&](int b, int ks) {
-            if constexpr (FP8KV)
-                return widen_fp8<F16>(kc[b][ks]);
-            else
-                return kc[b][ks];
+            return *(const u32x4 *)(krow + 32 * b * 256 + (((2 * ks + hl) ^ (lane & 15)) << 4));
         };
         auto vf = [&](int kk, int x) { return vfrag_lds(sV, kk, x, lane); };
         attend_tile<F16, NKB>(st, qf, kf, vf, u * UK, u >= n_full, lim, c2, lane);
@@ -871,17 +863,13 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, int bx, uint8_t *
     int u = u_begin + wv;
     if (u < u_end) {
         fetch_ids(u);
-        load_k(u, kA);
-        load_v(u);
+        load_kv(u);
         if (u + NW < u_end)
             fetch_ids(u + NW);
     }
     load_q(a, qf, row_ok, tok, head, lane);
-    for (; u < u_end; u += 2 * NW) {
-        step(u, kA, kB);
-        if (u + NW < u_end)
-            step(u + NW, kB, kA);
-    }
+    for (; u < u_end; u += NW)
+        step(u);
 
     // merge the waves' states: each wave writes (o, m, l) per lane, then wave
     // w < 4 combines d block w of every row and writes it
