@@ -37,7 +37,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="c2", choices=["c2", "c3", "c4", "c5"])
-    ap.add_argument("--splits", type=int, default=None, help="override num_splits (c3/c5)")
+    ap.add_argument("--splits", type=int, default=None, help="override num_splits (c3: default the planner's choice; c5: default 32)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the oracle CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -98,8 +98,16 @@ def build_calls(cfg: str, splits_override):
         return ("dense_fa2_fwd_b4_h32_n4096_d128_fp16_causal_and_full",
                 [("full", wl_f, 1), ("causal", wl_c, 1)])
     if cfg == "c3":
-        s = 8 if splits_override is None else splits_override
-        return (f"decode_paged_gqa_256seq_32q8kv_bs16_splits{s}", [("decode", wk.config3(), s)])
+        wl = wk.config3()
+        if splits_override is None:
+            # the split count the library's planner picks (host only)
+            import paged_varlen_flashattention_amd as ua
+            s = ua.auto_splits(wl.q, wl.k_cache, wl.v_cache, wl.q, wl.cu_seqlens_q, wl.seqused_k,
+                               wl.block_table, wl.max_seqlen_q, wl.max_seqlen_k, wl.softmax_scale,
+                               wl.causal)
+        else:
+            s = splits_override
+        return (f"decode_paged_gqa_256seq_32q8kv_bs16_splits{s}", [("decode", wl, s)])
     if cfg == "c4":
         return ("mixed_chunked_prefill_64dec_4x2048_64q8kv_bs32", [("mixed", wk.config4(), 1)])
     s = 32 if splits_override is None else splits_override

@@ -172,6 +172,17 @@ def plan(params: AttnParams) -> dict:
     return info.as_dict()
 
 
+def auto_splits(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table, max_seqlen_q,
+                max_seqlen_k, softmax_scale, causal, k_scale=None, v_scale=None) -> int:
+    """The split count the planner picks for num_splits = 0 given unlimited
+    workspace (host only, no device work)."""
+    probe = make_params(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table,
+                        max_seqlen_q, max_seqlen_k, softmax_scale, causal, k_scale, v_scale, 0,
+                        None, None)
+    probe.workspace, probe.workspace_bytes = 256, 1 << 62
+    return plan(probe)["num_splits"]
+
+
 def unified_attention(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table,
                       max_seqlen_q, max_seqlen_k, softmax_scale, causal, k_scale=None,
                       v_scale=None, num_splits=1, lse=None, workspace=None, stream=None):
@@ -187,12 +198,9 @@ def unified_attention(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_t
     if workspace is None and num_splits != 1:
         splits = num_splits
         if splits == 0:
-            # ask the planner what it would pick given unlimited workspace (host only)
-            probe = make_params(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table,
-                                max_seqlen_q, max_seqlen_k, softmax_scale, causal, k_scale,
-                                v_scale, 0, lse, None)
-            probe.workspace, probe.workspace_bytes = 256, 1 << 62
-            splits = plan(probe)["num_splits"]
+            splits = auto_splits(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table,
+                                 max_seqlen_q, max_seqlen_k, softmax_scale, causal, k_scale,
+                                 v_scale)
         nbytes = workspace_size(q.shape[0], q.shape[1], q.shape[2], splits)
         if nbytes:
             workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)

@@ -105,10 +105,13 @@ struct Plan {
 
 // Kernel choice: every sequence with q_len * G <= kDecodeRows rows goes to the
 // decode kernel; when max_seqlen_q * G <= kDecodeRows that is every sequence
-// and the prefill kernel is not launched.  Split choice for num_splits = 0:
-// enough workgroups for about two rounds over the CUs (two workgroups of 4
-// waves per CU), each split keeping at least 8 prefill tiles / 8 decode units,
-// within what the workspace holds.
+// and the prefill kernel is not launched.  Split choice for num_splits = 0,
+// within what the workspace holds and keeping at least 8 prefill tiles / 8
+// decode units per split: launches with prefill work aim at about two rounds
+// of workgroups over the CUs (two 4-wave workgroups per CU); decode-only
+// launches at about eight rounds, since their workgroups are short and
+// memory-bound and more of them balance uneven key lengths (on the 256 x
+// (1 query, 512..8192 keys) decode batch 2 splits stream best, 8 cost ~6%).
 Plan make_plan(const ua_attn_params *p) {
     Plan pl;
     const int G = p->num_q_heads / p->num_kv_heads;
@@ -130,7 +133,7 @@ Plan make_plan(const ua_attn_params *p) {
                     p->num_kv_heads;
             min_keys = 8 * ua::kPrefillTileN;
         }
-        const int64_t wg_wanted = 2LL * kNumCUs * 2;
+        const int64_t wg_wanted = (decode_only ? 8LL : 2LL) * kNumCUs * 2;
         int64_t want = units > 0 ? (wg_wanted + units - 1) / units : 1;
         const int64_t max_by_len = std::max<int64_t>(1, p->max_seqlen_k / min_keys);
         want = std::min<int64_t>({want, max_by_len, (int64_t)kMaxSplits});

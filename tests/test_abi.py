@@ -194,8 +194,13 @@ def test_auto_splits_respect_workspace(lib):
     p = base_params(num_splits=0, workspace=FAKE, workspace_bytes=small, **few)
     st, info = plan_status(lib, p)
     assert st == 0 and info.num_splits == 2
-    # plenty of workgroups already: no split even with room for one
+    # decode-only: about 8 rounds of 2 workgroups per CU over 256 CUs (4096);
+    # 256 x 8 (sequence, kv head) workgroups -> 2 splits, 4096 or more -> none
     p = base_params(num_splits=0, workspace=FAKE, workspace_bytes=1 << 40)
+    st, info = plan_status(lib, p)
+    assert st == 0 and info.num_splits == 2
+    many = dict(num_seqs=512, num_tokens=512)
+    p = base_params(num_splits=0, workspace=FAKE, workspace_bytes=1 << 40, **many)
     st, info = plan_status(lib, p)
     assert st == 0 and info.num_splits == 1
 
