@@ -250,7 +250,7 @@ ua_status ua_unified_attention(const ua_attn_params *p, void *stream) {
     a.short_to_decode = pl.decode ? 1 : 0;
     a.scale_log2 = p->softmax_scale * 1.44269504088896341f;
 
-    a.prefill_wgs = (int32_t)info.grid_x;
+    a.decode_wgs = (int32_t)info.decode_grid_x;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool f16 = p->q_dtype == UA_FP16, fp8 = p->kv_dtype == UA_FP8_E4M3FN, causal = p->causal != 0;

@@ -911,20 +911,21 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, int bx, uint8_t *
 
 // ------------------------------------------------------------------ the kernel
 
-// One launch for both paths: workgroups [0, prefill_wgs) run the prefill body,
-// the rest the decode body, so memory-bound decode work overlaps compute-bound
-// prefill work.  Two workgroups per CU whose waves pair up on each SIMD (wave
-// w of both on SIMD w), so the softmax of one wave overlaps the MFMAs of the
-// other.
+// One launch for both paths: workgroups [0, decode_wgs) run the decode body,
+// the rest the prefill body.  Decode workgroups come first so that, in a
+// mixed batch, their memory-bound streaming shares the CUs with the
+// compute-bound prefill workgroups from the start instead of trailing them.
+// Two workgroups per CU whose waves pair up on each SIMD (wave w of both on
+// SIMD w), so the softmax of one wave overlaps the MFMAs of the other.
 template <bool F16, bool FP8KV, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(const AttnArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[lds_bytes(kWaves)];
     const int bx = blockIdx.x;
-    if (bx < a.prefill_wgs)
-        prefill_body<F16, FP8KV, CAUSAL, SPLIT>(a, bx, lds);
+    if (bx < a.decode_wgs)
+        decode_body<F16, FP8KV, CAUSAL, SPLIT, kWaves>(a, bx, lds);
     else
-        decode_body<F16, FP8KV, CAUSAL, SPLIT, kWaves>(a, bx - a.prefill_wgs, lds);
+        prefill_body<F16, FP8KV, CAUSAL, SPLIT>(a, bx - a.decode_wgs, lds);
 }
 
 // ------------------------------------------------------------------ combine kernel

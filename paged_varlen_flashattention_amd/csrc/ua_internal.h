@@ -38,7 +38,7 @@ struct AttnArgs {
     int32_t num_splits;
     int32_t num_qslots;            // T / block_q + S
     int32_t short_to_decode;       // prefill body skips sequences with q_len * G <= kDecodeRows
-    int32_t prefill_wgs;           // workgroups [0, prefill_wgs) run the prefill body, the rest decode
+    int32_t decode_wgs;            // workgroups [0, decode_wgs) run the decode body, the rest prefill
     float scale_log2;              // softmax_scale * log2(e)
 };
 
@@ -47,8 +47,8 @@ constexpr int kPrefillTileN = 64;     // keys per prefill tile
 constexpr int kDecodeUnit = 32;       // keys per decode unit
 constexpr int kWaves = 4;             // wavefronts per workgroup, both bodies
 
-// Enqueue the attention kernel: grid.x = prefill workgroups (slots x Hkv) +
-// decode workgroups (S x Hkv), grid.y = splits.  q_f16: q/out are fp16 (else
+// Enqueue the attention kernel: grid.x = decode workgroups (S x Hkv) followed
+// by prefill workgroups (slots x Hkv), grid.y = splits.  q_f16: q/out are fp16 (else
 // bf16); kv_fp8: the cache holds fp8 e4m3fn codes (else the q dtype).
 hipError_t launch_attention(const AttnArgs &a, bool q_f16, bool kv_fp8, bool causal, bool split,
                             dim3 grid, hipStream_t stream);
