@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the oracle CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the measurements made after the timed region (cold-cache call "
+                         "times, c3 split sweep, c4 sub-batches)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of --copy-bytes bytes (counter calibration)")
     ap.add_argument("--copy-bytes", type=int, default=1 << 30)
@@ -230,9 +233,97 @@ def main():
         if label != dominant:
             result[f"roofline_{label}"] = roofline(label, f"{args.config}_{label}")
 
+    if not args.no_extras:
+        extras(args, prepared, per, result, call, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(prepared, compute_bound, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def time_calls(fn, n: int, stream, flush=None):
+    """Per-call durations (ms) of n calls of fn, each bracketed by HIP events on
+    `stream`; with `flush`, it runs before every call, outside the events."""
+    import numpy as np
+    import torch
+    durs = []
+    for _ in range(n):
+        if flush is not None:
+            flush()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        durs.append(e0.elapsed_time(e1))
+    return np.array(durs)
+
+
+def extras(args, prepared, per, result, call, stream) -> None:
+    """Measurements made after the timed region (they do not enter `value`):
+    per-call times with L2/MALL flushed before each call (a 512 MB write), the
+    decode batch at splits 1/2/4/8, and the mixed batch's prefill-only and
+    decode-only sub-batches with its roofline time max(F/P_mfma, B_KV/P_hbm)."""
+    import numpy as np
+    import torch
+
+    import workloads as wk
+    dev = torch.device("cuda:0")
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    flush = lambda: scrub.fill_(1)
+    for label, wl, splits, d, ws in prepared:
+        t = time_calls(lambda: call(wl, splits, d, ws), 10, stream, flush)
+        per_r = result["per_call"][label]
+        per_r["ms_cold_median"] = round(float(np.median(t)), 4)
+        per_r["ms_cold_min"] = round(float(t.min()), 4)
+
+    def run_sub(wl, splits):
+        d = {"q": wl.q.to(dev), "k": wl.k_cache.to(dev), "v": wl.v_cache.to(dev),
+             "cu": wl.cu_seqlens_q.to(dev), "kv": wl.seqused_k.to(dev), "bt": wl.block_table.to(dev),
+             "ks": None if wl.k_scale is None else torch.tensor([wl.k_scale], device=dev),
+             "vs": None if wl.v_scale is None else torch.tensor([wl.v_scale], device=dev)}
+        d["out"] = torch.empty_like(d["q"])
+        import paged_varlen_flashattention_amd as ua
+        ws = None
+        if splits > 1:
+            ws = torch.empty(ua.workspace_size(wl.num_tokens, wl.num_q_heads, 128, splits),
+                             dtype=torch.uint8, device=dev)
+        fn = lambda: call(wl, splits, d, ws)
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        t = time_calls(fn, 20, stream)
+        return float(np.median(t)), float(t.min())
+
+    if args.config == "c3":
+        wl = prepared[0][1]
+        sweep = []
+        for sp in (1, 2, 4, 8):
+            med, mn = run_sub(wl, sp)
+            sweep.append({"splits": sp, "ms_median": round(med, 4), "ms_min": round(mn, 4),
+                          "GB/s": round(wl.kv_bytes() / (med * 1e-3) / 1e9, 1),
+                          "hbm_frac": round(wl.kv_bytes() / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)})
+        result["splits_sweep"] = sweep
+    if args.config == "c4":
+        wl = prepared[0][1]
+        ql = wl.q_lens
+        dec = wk.subset(wl, [s for s in range(len(ql)) if ql[s] == 1], "c4_decode_part")
+        pre = wk.subset(wl, [s for s in range(len(ql)) if ql[s] > 1], "c4_prefill_part")
+        med_d, _ = run_sub(dec, 1)
+        med_p, _ = run_sub(pre, 1)
+        t_mfma = wl.flops() / (PEAK_MFMA_TFLOPS * 1e12) * 1e6
+        t_hbm = wl.kv_bytes() / (PEAK_HBM_GBS * 1e9) * 1e6
+        t_roof = max(t_mfma, t_hbm)
+        meas = per[prepared[0][0]]["ms_median"] * 1e3
+        result["sub_batches"] = {
+            "decode_only": {"ms_median": round(med_d, 4),
+                            "GB/s": round(dec.kv_bytes() / (med_d * 1e-3) / 1e9, 1),
+                            "hbm_frac": round(dec.kv_bytes() / (med_d * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+            "prefill_only": {"ms_median": round(med_p, 4),
+                             "TFLOP/s": round(pre.flops() / (med_p * 1e-3) / 1e12, 1),
+                             "mfma_frac": round(pre.flops() / (med_p * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4)},
+            "t_roof_us": round(t_roof, 1), "t_roof_mfma_us": round(t_mfma, 1),
+            "t_roof_hbm_us": round(t_hbm, 1), "measured_us": round(meas, 1),
+            "frac_of_roof": round(t_roof / meas, 4)}
 
 
 def cpu_baseline(prepared, compute_bound: bool, target_s: float) -> dict:

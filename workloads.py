@@ -339,6 +339,20 @@ def config5(num_splits: int = 32, kv_len: int = 131072) -> Workload:
                       num_splits=num_splits)
 
 
+def subset(wl: Workload, seqs: Sequence[int], name: Optional[str] = None) -> Workload:
+    """The sub-batch made of the given sequences (same caches and table rows;
+    their query rows repacked in order)."""
+    cu = wl.cu_seqlens_q.numpy().astype(np.int64)
+    rows = np.concatenate([np.arange(cu[s], cu[s + 1]) for s in seqs]).astype(np.int64)
+    lens = [int(cu[s + 1] - cu[s]) for s in seqs]
+    new_cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32)
+    idx = torch.as_tensor(np.asarray(seqs, dtype=np.int64))
+    return Workload(**{**wl.__dict__, "name": name or f"{wl.name}_subset",
+                       "q": wl.q[torch.as_tensor(rows)].contiguous(), "cu_seqlens_q": new_cu,
+                       "seqused_k": wl.seqused_k[idx].contiguous(),
+                       "block_table": wl.block_table[idx].contiguous(), "meta": dict(wl.meta)})
+
+
 CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
 
 
