@@ -36,7 +36,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="c2", choices=["c2", "c3", "c4", "c5"])
+    ap.add_argument("--config", default="c2", choices=["c2", "c3", "c4", "c5", "append"])
     ap.add_argument("--splits", type=int, default=None, help="override num_splits (c3: default the planner's choice; c5: default 32)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the oracle CPU-baseline sample")
@@ -128,6 +128,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(args.copy_bytes)
+        return
+    if args.config == "append":
+        main_append(args)
         return
 
     import numpy as np
@@ -238,6 +241,116 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(prepared, compute_bound, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def append_bytes(k_new, k_cache) -> int:
+    """Algorithmic bytes of an append: every new k and v element read once and
+    written once in the cache dtype."""
+    return int(k_new.numel() * 2 * (k_new.element_size() + k_cache.element_size()))
+
+
+def main_append(args) -> None:
+    """KV-cache append (ua_kv_append): the dense batch's 4 x 4096 new tokens x
+    32 kv heads (fp16) written into its paged cache (every position of the
+    cache is a new token there).  Value: algorithmic GB/s (read + write)."""
+    import numpy as np
+    import torch
+
+    import paged_varlen_flashattention_amd as ua
+    import workloads as wk
+    if not torch.cuda.is_available():
+        raise RuntimeError("bench.py needs a GPU")
+    ua.load_library()
+    dev = torch.device("cuda:0")
+    wl = wk.config2(causal=True)
+    # the new rows are the batch's k and v rows in token order (q has the same shape)
+    k_new = wl.q.to(dev)
+    v_new = torch.flip(wl.q, dims=[2]).contiguous().to(dev)
+    k_cache = torch.empty_like(wl.k_cache, device=dev)
+    v_cache = torch.empty_like(wl.v_cache, device=dev)
+    cu, kv, bt = wl.cu_seqlens_q.to(dev), wl.seqused_k.to(dev), wl.block_table.to(dev)
+    stream = torch.cuda.current_stream()
+    fn = lambda: ua.kv_append(k_new, v_new, k_cache, v_cache, cu, kv, bt, stream=stream)
+    for _ in range(args.warmup):
+        fn()
+    torch.cuda.synchronize()
+    K = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for e0, e1 in evs:
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / K
+    durs = np.array([a.elapsed_time(b) for a, b in evs])
+    nbytes = append_bytes(k_new, k_cache)
+    value = nbytes / (ms_step * 1e-3) / 1e9
+    ach = nbytes / (durs.mean() * 1e-3) / 1e9
+    result = {
+        "metric": "KV-append GB/s (read + write)", "value": round(value, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp16",
+        "data": "synthetic (seeded N(0,1) rows, paged cache)",
+        "config": {"workload": "kv_append_b4_n4096_kvh32_d128_fp16_bs16", "tokens": int(k_new.shape[0]),
+                   "kv_heads": int(k_new.shape[1])},
+        "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic_from_profiles("append_bulk"),
+                     "launch_ms_mean": round(float(durs.mean()), 4)},
+        "per_call": {"append": {"ms_mean": round(float(durs.mean()), 4), "ms_min": round(float(durs.min()), 4),
+                                "ms_median": round(float(np.median(durs)), 4), "bytes": nbytes}},
+    }
+    if not args.no_extras:
+        # the mixed batch's 8256 new tokens x 8 kv heads, into a bf16 and an fp8 cache
+        w4 = wk.config4()
+        kn4 = w4.q[:, :8].contiguous().to(dev)
+        vn4 = w4.q[:, 8:16].contiguous().to(dev)
+        cu4, kv4, bt4 = w4.cu_seqlens_q.to(dev), w4.seqused_k.to(dev), w4.block_table.to(dev)
+        mixed = {}
+        for name, cdt in (("bf16", torch.bfloat16), ("fp8_e4m3fn", torch.float8_e4m3fn)):
+            kc4 = torch.empty(w4.k_cache.shape, dtype=cdt, device=dev)
+            vc4 = torch.empty_like(kc4)
+            sc = torch.tensor([0.01], dtype=torch.float32, device=dev) if cdt == torch.float8_e4m3fn else None
+            f4 = lambda: ua.kv_append(kn4, vn4, kc4, vc4, cu4, kv4, bt4, sc, sc, stream=stream)
+            for _ in range(3):
+                f4()
+            torch.cuda.synchronize()
+            t = time_calls(f4, 20, stream)
+            b4 = append_bytes(kn4, kc4)
+            mixed[name] = {"ms_median": round(float(np.median(t)), 4),
+                           "GB/s": round(b4 / (np.median(t) * 1e-3) / 1e9, 1), "bytes": b4}
+        result["mixed_batch_append"] = mixed
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_append(wl, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline_append(wl, target_s: float) -> dict:
+    """The append oracle, as it stands, on a bounded sample of the same batch:
+    whole sequences appended one call each, cycling over the batch until about
+    target_s seconds; GB/s of algorithmic bytes."""
+    import torch
+
+    import oracle.append as oa
+    work, elapsed, calls = 0, 0.0, 0
+    cu = wl.cu_seqlens_q.numpy()
+    S = len(cu) - 1
+    while elapsed < target_s:
+        s = calls % S
+        n = int(cu[s + 1] - cu[s])
+        t0 = time.perf_counter()
+        oa.kv_append(wl.q[cu[s]:cu[s + 1]], wl.q[cu[s]:cu[s + 1]], torch.tensor([0, n], dtype=torch.int32),
+                     wl.seqused_k[s:s + 1], wl.block_table[s:s + 1], wl.k_cache, wl.v_cache)
+        elapsed += time.perf_counter() - t0
+        work += n * wl.q.shape[1] * wl.q.shape[2] * 2 * (2 + 2)
+        calls += 1
+    return {"value": round(work / elapsed / 1e9, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{calls} whole-sequence appends ({n} tokens x {wl.q.shape[1]} kv heads each) of the "
+                      f"same batch by the numpy oracle (single thread; each call also copies the caches it "
+                      f"returns), {elapsed:.1f} s on {platform.processor() or 'host'}"}
 
 
 def time_calls(fn, n: int, stream, flush=None):

@@ -197,6 +197,67 @@ size_t ua_workspace_size(int32_t num_tokens, int32_t num_q_heads, int32_t head_s
  * Validates *p exactly as ua_unified_attention does. */
 ua_status ua_plan(const ua_attn_params *p, ua_plan_info *plan);
 
+/*
+ * KV-cache append (page "flashatten takeaways EP2 工程", section "kv cache":
+ * the cache of a sequence grows by the new tokens' k and v rows; section
+ * "源代码接口": the split-KV launch's Append_KV switch).  Writes the k and v
+ * rows of the new tokens into their page slots, converted to the cache dtype:
+ * token i of sequence s (packed row cu_seqlens_q[s] + i, i < q_len(s)) sits
+ * at key position kv_len(s) - q_len(s) + i (the newest positions, as in the
+ * causal convention of ua_attn_params), i.e. in physical block
+ * block_table[s * W + pos / bs], slot pos % bs.
+ *
+ * k_new,       [T, Hkv, D] of new_dtype (bf16 or fp16); strides
+ * v_new        new_stride_token, new_stride_head (elements).
+ * k_cache,     [NB, bs, Hkv, D] of cache_dtype (new_dtype, or fp8 e4m3fn);
+ * v_cache      strides kv_stride_block, kv_stride_slot, kv_stride_head.
+ *              Only the appended rows are written.
+ * cu_seqlens_q [S + 1] int32 as in ua_attn_params (new tokens per sequence).
+ * seqused_k    [S] int32: kv_len(s) AFTER the append (>= q_len(s)).
+ * block_table  [S, W] int32; the pages holding the new positions must be
+ *              allocated by the caller.
+ * k_scale,     device fp32 scalars, required iff cache_dtype is fp8 (else
+ * v_scale      NULL): a value x is stored as the e4m3fn code nearest to
+ *              x / scale (round to nearest, ties to even), saturated to +-448.
+ *
+ * Requirements checked on the host: abi_version == UA_ABI_VERSION; non-NULL
+ * k_new, v_new, k_cache, v_cache, cu_seqlens_q, seqused_k, block_table (when
+ * S > 0 and T > 0); D == 128; bs a power of two in [16, 4096]; strides
+ * multiples of 8 and positive; 16-byte aligned data pointers.  Rows of tokens
+ * that belong to no sequence are not read.  S == 0 or T == 0 is a no-op.
+ * Data-dependent violations (positions past the table, block ids outside
+ * [0, NB), overlapping sequences) are undefined behaviour.
+ */
+typedef struct ua_append_params {
+    uint32_t abi_version;
+    int32_t new_dtype;               /* ua_dtype of k_new and v_new */
+    int32_t cache_dtype;             /* ua_dtype of k_cache and v_cache */
+    int32_t reserved;
+
+    const void *k_new;
+    const void *v_new;
+    void *k_cache;
+    void *v_cache;
+    const int32_t *cu_seqlens_q;
+    const int32_t *seqused_k;
+    const int32_t *block_table;
+    const float *k_scale;
+    const float *v_scale;
+
+    int64_t new_stride_token, new_stride_head;
+    int64_t kv_stride_block, kv_stride_slot, kv_stride_head;
+
+    int32_t num_seqs, num_tokens, num_kv_heads, head_size;
+    int32_t block_size, num_blocks, block_table_stride;
+    int32_t reserved2;
+} ua_append_params;
+
+/* Enqueue the append kernel on `stream`.  Returns UA_OK once enqueued. */
+ua_status ua_kv_append(const ua_append_params *p, void *stream);
+
+/* sizeof(ua_append_params) of the built library. */
+size_t ua_append_params_size(void);
+
 /* Static text for a status code. */
 const char *ua_status_string(int32_t status);
 

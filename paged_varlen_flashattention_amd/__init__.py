@@ -8,11 +8,12 @@ else.  Calls raise when libua.so is missing; there is no CPU path.
 """
 from ._binding import (ABI_VERSION, EXPORTS, LIB_PATH, UA_BF16, UA_ERR_HIP, UA_ERR_INVALID_ARG,
                        UA_ERR_UNSUPPORTED, UA_ERR_WORKSPACE, UA_FP16, UA_FP8_E4M3FN, UA_OK,
-                       AttnParams, PlanInfo, UAError, auto_splits, load_library, make_params, plan,
+                       AppendParams, AttnParams, PlanInfo, UAError, auto_splits, kv_append,
+                       load_library, make_append_params, make_params, plan,
                        split_kv_combine, status_string, unified_attention, workspace_size)
 
-__all__ = ["ABI_VERSION", "EXPORTS", "LIB_PATH", "AttnParams", "PlanInfo", "UAError",
-           "auto_splits", "load_library", "make_params", "plan", "split_kv_combine", "status_string",
+__all__ = ["ABI_VERSION", "EXPORTS", "LIB_PATH", "AppendParams", "AttnParams", "PlanInfo",
+           "UAError", "auto_splits", "kv_append", "make_append_params", "load_library", "make_params", "plan", "split_kv_combine", "status_string",
            "unified_attention", "workspace_size", "UA_OK", "UA_ERR_INVALID_ARG",
            "UA_ERR_UNSUPPORTED", "UA_ERR_WORKSPACE", "UA_ERR_HIP", "UA_BF16", "UA_FP16",
            "UA_FP8_E4M3FN"]

@@ -23,7 +23,8 @@ _DTYPES = {torch.bfloat16: UA_BF16, torch.float16: UA_FP16, torch.float8_e4m3fn:
 
 # Every symbol include/ua.h declares.
 EXPORTS = ("ua_unified_attention", "ua_split_kv_combine", "ua_workspace_size", "ua_plan",
-           "ua_status_string", "ua_abi_version", "ua_params_size", "ua_plan_info_size")
+           "ua_status_string", "ua_abi_version", "ua_params_size", "ua_plan_info_size",
+           "ua_kv_append", "ua_append_params_size")
 
 
 class UAError(RuntimeError):
@@ -52,6 +53,25 @@ class AttnParams(ctypes.Structure):
         ("num_blocks", ctypes.c_int32), ("block_table_stride", ctypes.c_int32),
         ("max_seqlen_q", ctypes.c_int32), ("max_seqlen_k", ctypes.c_int32),
         ("num_splits", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+    ]
+
+
+class AppendParams(ctypes.Structure):
+    """Mirror of ua_append_params (field order and types as in include/ua.h)."""
+    _fields_ = [
+        ("abi_version", ctypes.c_uint32), ("new_dtype", ctypes.c_int32),
+        ("cache_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("k_new", ctypes.c_void_p), ("v_new", ctypes.c_void_p),
+        ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
+        ("cu_seqlens_q", ctypes.c_void_p), ("seqused_k", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p), ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+        ("new_stride_token", ctypes.c_int64), ("new_stride_head", ctypes.c_int64),
+        ("kv_stride_block", ctypes.c_int64), ("kv_stride_slot", ctypes.c_int64),
+        ("kv_stride_head", ctypes.c_int64),
+        ("num_seqs", ctypes.c_int32), ("num_tokens", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32), ("head_size", ctypes.c_int32),
+        ("block_size", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
+        ("block_table_stride", ctypes.c_int32), ("reserved2", ctypes.c_int32),
     ]
 
 
@@ -95,10 +115,14 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.ua_abi_version.restype = ctypes.c_uint32
     lib.ua_params_size.restype = ctypes.c_size_t
     lib.ua_plan_info_size.restype = ctypes.c_size_t
+    lib.ua_kv_append.argtypes = [ctypes.POINTER(AppendParams), vp]
+    lib.ua_kv_append.restype = ctypes.c_int
+    lib.ua_append_params_size.restype = ctypes.c_size_t
     if lib.ua_abi_version() != ABI_VERSION:
         raise RuntimeError("libua.so ABI version mismatch")
     if lib.ua_params_size() != ctypes.sizeof(AttnParams) or \
-            lib.ua_plan_info_size() != ctypes.sizeof(PlanInfo):
+            lib.ua_plan_info_size() != ctypes.sizeof(PlanInfo) or \
+            lib.ua_append_params_size() != ctypes.sizeof(AppendParams):
         raise RuntimeError("libua.so struct layout differs from the binding")
     if path is None:
         _lib = lib
@@ -210,6 +234,47 @@ def unified_attention(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_t
     if st != UA_OK:
         raise UAError(st, "ua_unified_attention")
     return out
+
+
+def make_append_params(k_new, v_new, k_cache, v_cache, cu_seqlens_q, seqused_k, block_table,
+                       k_scale=None, v_scale=None) -> AppendParams:
+    """Fill ua_append_params from tensors (no copies, no device work)."""
+    p = AppendParams()
+    p.abi_version = ABI_VERSION
+    p.new_dtype = _DTYPES.get(k_new.dtype, 99)
+    p.cache_dtype = _DTYPES.get(k_cache.dtype, 99)
+    p.k_new, p.v_new = k_new.data_ptr(), v_new.data_ptr()
+    p.k_cache, p.v_cache = k_cache.data_ptr(), v_cache.data_ptr()
+    p.cu_seqlens_q, p.seqused_k = cu_seqlens_q.data_ptr(), seqused_k.data_ptr()
+    p.block_table = block_table.data_ptr()
+    p.k_scale, p.v_scale = _ptr(k_scale), _ptr(v_scale)
+    if k_new.stride() != v_new.stride():
+        raise ValueError("k_new and v_new must share strides")
+    if k_cache.stride() != v_cache.stride():
+        raise ValueError("k_cache and v_cache must share strides")
+    p.new_stride_token, p.new_stride_head = k_new.stride(0), k_new.stride(1)
+    p.kv_stride_block, p.kv_stride_slot, p.kv_stride_head = k_cache.stride(0), k_cache.stride(1), k_cache.stride(2)
+    p.num_seqs = seqused_k.numel()
+    p.num_tokens = k_new.shape[0]
+    p.num_kv_heads = k_new.shape[1]
+    p.head_size = k_new.shape[2]
+    p.block_size = k_cache.shape[1]
+    p.num_blocks = k_cache.shape[0]
+    p.block_table_stride = block_table.stride(0) if block_table.dim() == 2 else block_table.numel()
+    return p
+
+
+def kv_append(k_new, v_new, k_cache, v_cache, cu_seqlens_q, seqused_k, block_table,
+              k_scale=None, v_scale=None, stream=None):
+    """ua_kv_append on torch device tensors: writes the new tokens' rows of
+    k_new / v_new [T, Hkv, 128] (bf16/fp16) into k_cache / v_cache
+    [NB, bs, Hkv, 128] (same dtype, or float8_e4m3fn with 1-element fp32
+    k_scale / v_scale) at positions seqused_k - q_len + i."""
+    p = make_append_params(k_new, v_new, k_cache, v_cache, cu_seqlens_q, seqused_k, block_table,
+                           k_scale, v_scale)
+    st = load_library().ua_kv_append(ctypes.byref(p), _stream_handle(stream))
+    if st != UA_OK:
+        raise UAError(st, "ua_kv_append")
 
 
 def split_kv_combine(o_partial, lse_partial, out, lse=None, stream=None):

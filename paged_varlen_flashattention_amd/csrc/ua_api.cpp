@@ -146,6 +146,43 @@ Plan make_plan(const ua_attn_params *p) {
     return pl;
 }
 
+// Host-checkable requirements of ua_kv_append (see ua.h).
+ua_status validate_append(const ua_append_params *p) {
+    if (p == nullptr || p->abi_version != UA_ABI_VERSION)
+        return UA_ERR_INVALID_ARG;
+    if (p->num_seqs < 0 || p->num_tokens < 0 || p->num_kv_heads <= 0 || p->num_blocks < 0 ||
+        p->block_table_stride < 0)
+        return UA_ERR_INVALID_ARG;
+    if (p->new_dtype != UA_BF16 && p->new_dtype != UA_FP16)
+        return p->new_dtype == UA_FP8_E4M3FN ? UA_ERR_UNSUPPORTED : UA_ERR_INVALID_ARG;
+    if (p->cache_dtype != p->new_dtype && p->cache_dtype != UA_FP8_E4M3FN)
+        return (p->cache_dtype == UA_BF16 || p->cache_dtype == UA_FP16) ? UA_ERR_UNSUPPORTED
+                                                                        : UA_ERR_INVALID_ARG;
+    if (p->head_size != ua::kHeadSize)
+        return UA_ERR_UNSUPPORTED;
+    if (!pow2(p->block_size) || p->block_size < 16 || p->block_size > 4096)
+        return UA_ERR_INVALID_ARG;
+    if (p->num_seqs == 0 || p->num_tokens == 0)
+        return UA_OK;
+    if (!p->k_new || !p->v_new || !p->k_cache || !p->v_cache || !p->cu_seqlens_q || !p->seqused_k ||
+        !p->block_table)
+        return UA_ERR_INVALID_ARG;
+    const bool fp8 = p->cache_dtype == UA_FP8_E4M3FN;
+    if (fp8 && (!p->k_scale || !p->v_scale))
+        return UA_ERR_INVALID_ARG;
+    const int64_t strides[] = {p->new_stride_token, p->new_stride_head, p->kv_stride_block,
+                               p->kv_stride_slot, p->kv_stride_head};
+    for (int64_t st : strides)
+        if (st <= 0 || st % 8 != 0)
+            return UA_ERR_INVALID_ARG;
+    if (!aligned(p->k_new, 16) || !aligned(p->v_new, 16) || !aligned(p->k_cache, 16) ||
+        !aligned(p->v_cache, 16))
+        return UA_ERR_INVALID_ARG;
+    if ((int64_t)p->num_tokens * p->num_kv_heads > (int64_t)0x7fffffff * 16)
+        return UA_ERR_UNSUPPORTED;
+    return UA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -153,6 +190,39 @@ extern "C" {
 uint32_t ua_abi_version(void) { return UA_ABI_VERSION; }
 size_t ua_params_size(void) { return sizeof(ua_attn_params); }
 size_t ua_plan_info_size(void) { return sizeof(ua_plan_info); }
+size_t ua_append_params_size(void) { return sizeof(ua_append_params); }
+
+ua_status ua_kv_append(const ua_append_params *p, void *stream) {
+    const ua_status st = validate_append(p);
+    if (st != UA_OK)
+        return st;
+    if (p->num_seqs == 0 || p->num_tokens == 0)
+        return UA_OK;
+    ua::AppendArgs a{};
+    a.k_new = p->k_new;
+    a.v_new = p->v_new;
+    a.k_cache = p->k_cache;
+    a.v_cache = p->v_cache;
+    a.cu_seqlens_q = p->cu_seqlens_q;
+    a.seqused_k = p->seqused_k;
+    a.block_table = p->block_table;
+    a.k_scale = p->cache_dtype == UA_FP8_E4M3FN ? p->k_scale : nullptr;
+    a.v_scale = p->cache_dtype == UA_FP8_E4M3FN ? p->v_scale : nullptr;
+    a.new_st_tok = p->new_stride_token;
+    a.new_st_head = p->new_stride_head;
+    a.kv_st_blk = p->kv_stride_block;
+    a.kv_st_slot = p->kv_stride_slot;
+    a.kv_st_head = p->kv_stride_head;
+    a.bt_stride = p->block_table_stride;
+    a.num_seqs = p->num_seqs;
+    a.num_tokens = p->num_tokens;
+    a.num_kv_heads = p->num_kv_heads;
+    a.log2_block_size = ilog2(p->block_size);
+    if (ua::launch_append(a, p->new_dtype == UA_FP16, p->cache_dtype == UA_FP8_E4M3FN,
+                          static_cast<hipStream_t>(stream)) != hipSuccess)
+        return UA_ERR_HIP;
+    return UA_OK;
+}
 
 const char *ua_status_string(int32_t status) {
     switch (status) {

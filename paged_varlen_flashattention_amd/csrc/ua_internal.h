@@ -59,4 +59,26 @@ hipError_t launch_combine(const float *o_part, const float *lse_part, int32_t nu
                           int64_t o_st_tok, int64_t o_st_head, float *lse_out,
                           hipStream_t stream);
 
+// Arguments of the KV-cache append kernel.
+struct AppendArgs {
+    const void *k_new;
+    const void *v_new;
+    void *k_cache;
+    void *v_cache;
+    const int32_t *cu_seqlens_q;
+    const int32_t *seqused_k;
+    const int32_t *block_table;
+    const float *k_scale;          // fp8 cache only
+    const float *v_scale;
+    int64_t new_st_tok, new_st_head;
+    int64_t kv_st_blk, kv_st_slot, kv_st_head;
+    int64_t bt_stride;
+    int32_t num_seqs, num_tokens, num_kv_heads;
+    int32_t log2_block_size;
+};
+
+// Enqueue the append kernel over T * Hkv rows.  new_f16: k_new/v_new are fp16
+// (else bf16); cache_fp8: the cache holds fp8 e4m3fn codes (else new dtype).
+hipError_t launch_append(const AppendArgs &a, bool new_f16, bool cache_fp8, hipStream_t stream);
+
 }  // namespace ua

@@ -251,3 +251,63 @@ def test_combine_invalid_arguments(lib, args, status):
 def test_binding_raises_without_library(tmp_path):
     with pytest.raises(RuntimeError, match="missing"):
         B.load_library(str(tmp_path / "nope.so"))
+
+
+# ------------------------------------------------------------------ ua_kv_append (host checks only)
+
+def append_params(**kw):
+    """A valid ua_append_params set with fake addresses (never launched here)."""
+    p = B.AppendParams()
+    p.abi_version = B.ABI_VERSION
+    p.new_dtype = p.cache_dtype = B.UA_BF16
+    for name in ("k_new", "v_new", "k_cache", "v_cache", "cu_seqlens_q", "seqused_k", "block_table"):
+        setattr(p, name, FAKE)
+    S, Hkv, D, bs = 4, 8, 128, 16
+    p.num_seqs, p.num_tokens, p.num_kv_heads, p.head_size = S, 64, Hkv, D
+    p.block_size, p.num_blocks, p.block_table_stride = bs, 1024, 64
+    p.new_stride_token, p.new_stride_head = Hkv * D, D
+    p.kv_stride_block, p.kv_stride_slot, p.kv_stride_head = bs * Hkv * D, Hkv * D, D
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def test_append_struct_layout(lib):
+    assert lib.ua_append_params_size() == ctypes.sizeof(B.AppendParams) == 160
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("abi_version", 3, B.UA_ERR_INVALID_ARG),
+    ("num_seqs", -1, B.UA_ERR_INVALID_ARG),
+    ("num_tokens", -2, B.UA_ERR_INVALID_ARG),
+    ("num_kv_heads", 0, B.UA_ERR_INVALID_ARG),
+    ("head_size", 64, B.UA_ERR_UNSUPPORTED),
+    ("block_size", 24, B.UA_ERR_INVALID_ARG),
+    ("block_size", 8, B.UA_ERR_INVALID_ARG),
+    ("new_dtype", B.UA_FP8_E4M3FN, B.UA_ERR_UNSUPPORTED),
+    ("new_dtype", 7, B.UA_ERR_INVALID_ARG),
+    ("cache_dtype", B.UA_FP16, B.UA_ERR_UNSUPPORTED),          # bf16 rows into an fp16 cache
+    ("cache_dtype", 9, B.UA_ERR_INVALID_ARG),
+    ("k_new", None, B.UA_ERR_INVALID_ARG),
+    ("v_cache", None, B.UA_ERR_INVALID_ARG),
+    ("block_table", None, B.UA_ERR_INVALID_ARG),
+    ("new_stride_head", 100, B.UA_ERR_INVALID_ARG),
+    ("kv_stride_slot", 0, B.UA_ERR_INVALID_ARG),
+    ("k_cache", FAKE + 8, B.UA_ERR_INVALID_ARG),               # not 16-byte aligned
+])
+def test_append_invalid_args(lib, field, value, status):
+    p = append_params(**{field: value})
+    assert lib.ua_kv_append(ctypes.byref(p), None) == status
+
+
+def test_append_fp8_needs_scales(lib):
+    p = append_params(cache_dtype=B.UA_FP8_E4M3FN)
+    assert lib.ua_kv_append(ctypes.byref(p), None) == B.UA_ERR_INVALID_ARG
+    p = append_params(cache_dtype=B.UA_FP8_E4M3FN, k_scale=FAKE)
+    assert lib.ua_kv_append(ctypes.byref(p), None) == B.UA_ERR_INVALID_ARG
+
+
+def test_append_empty_batch_is_noop(lib):
+    assert lib.ua_kv_append(ctypes.byref(append_params(num_tokens=0, k_new=None)), None) == B.UA_OK
+    assert lib.ua_kv_append(ctypes.byref(append_params(num_seqs=0, block_table=None)), None) == B.UA_OK
+    assert lib.ua_kv_append(None, None) == B.UA_ERR_INVALID_ARG

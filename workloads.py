@@ -353,6 +353,56 @@ def subset(wl: Workload, seqs: Sequence[int], name: Optional[str] = None) -> Wor
                        "block_table": wl.block_table[idx].contiguous(), "meta": dict(wl.meta)})
 
 
+def append_case(seed: int, *, num_seqs: int = 4, max_new: int = 40, max_prefix: int = 100,
+                kv_heads: int = 2, block_size: int = 16, new_dtype: str = "bf16",
+                cache_dtype: Optional[str] = None, saturate: bool = False) -> dict:
+    """Seeded inputs of a KV-cache append (CPU tensors): new rows k_new / v_new
+    [T, Hkv, 128] (N(0,1) x 3), lengths (q_len U{0..max_new}, at least one > 0;
+    kv_len = prefix U{0..max_prefix} + q_len), permuted page tables (entries past
+    each sequence's last page poisoned with -1), caches filled with unrelated
+    values (finite fp8 codes for an fp8 cache), and for an fp8 cache per-tensor
+    scales amax / 448 (or amax / 600 with `saturate`, so that some values
+    exceed the largest code)."""
+    cache_dtype = cache_dtype or new_dtype
+    rng = _seed(4000 + seed, STREAM_LENGTHS)
+    q_lens = rng.integers(0, max_new + 1, size=num_seqs)
+    if q_lens.max() == 0:
+        q_lens[0] = 1
+    kv_lens = rng.integers(0, max_prefix + 1, size=num_seqs) + q_lens
+    pages = np.maximum(1, (kv_lens + block_size - 1) // block_size)
+    W = int(pages.max())
+    NB = int(pages.sum()) + 7
+    ids = rng.permutation(NB)
+    bt = np.full((num_seqs, W), -1, dtype=np.int32)
+    at = 0
+    for s in range(num_seqs):
+        bt[s, :pages[s]] = ids[at:at + pages[s]]
+        at += pages[s]
+    T = int(q_lens.sum())
+    D = 128
+    g = _seed(4000 + seed, STREAM_K)
+    tdt = TORCH_DTYPES[new_dtype]
+    k_new = torch.from_numpy((g.standard_normal((T, kv_heads, D)) * 3).astype(np.float32)).to(tdt)
+    v_new = torch.from_numpy((g.standard_normal((T, kv_heads, D)) * 3).astype(np.float32)).to(tdt)
+    shape = (NB, block_size, kv_heads, D)
+    if cache_dtype == "fp8_e4m3fn":
+        codes = g.integers(0, 0x7F, size=shape, dtype=np.uint8) | (g.integers(0, 2, size=shape, dtype=np.uint8) << 7)
+        k_cache = torch.from_numpy(codes).view(torch.float8_e4m3fn)
+        codes = g.integers(0, 0x7F, size=shape, dtype=np.uint8) | (g.integers(0, 2, size=shape, dtype=np.uint8) << 7)
+        v_cache = torch.from_numpy(codes).view(torch.float8_e4m3fn)
+        div = 600.0 if saturate else FP8_MAX
+        k_scale = float(k_new.float().abs().max()) / div if T else 1.0
+        v_scale = float(v_new.float().abs().max()) / div if T else 1.0
+    else:
+        k_cache = torch.from_numpy(g.standard_normal(shape).astype(np.float32)).to(TORCH_DTYPES[cache_dtype])
+        v_cache = torch.from_numpy(g.standard_normal(shape).astype(np.float32)).to(TORCH_DTYPES[cache_dtype])
+        k_scale = v_scale = None
+    return {"k_new": k_new, "v_new": v_new,
+            "cu_seqlens_q": torch.tensor(np.concatenate([[0], np.cumsum(q_lens)]), dtype=torch.int32),
+            "seqused_k": torch.tensor(kv_lens, dtype=torch.int32), "block_table": torch.from_numpy(bt),
+            "k_cache": k_cache, "v_cache": v_cache, "k_scale": k_scale, "v_scale": v_scale}
+
+
 CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
 
 
