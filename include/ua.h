@@ -147,12 +147,16 @@ typedef struct ua_attn_params {
  * share each 64-key tile) and the decode kernel (every sequence with
  * q_len * (Hq / Hkv) <= 32 query rows: 4 waves stream disjoint 32-key units
  * and merge).  When max_seqlen_q * (Hq / Hkv) <= 32 only the decode kernel
- * runs; otherwise both run and the prefill kernel skips the short sequences. */
+ * runs; otherwise both run and the prefill kernel skips the short sequences.
+ * Split launches with prefill work use 8-wave workgroups: two groups of 4
+ * prefill waves take alternate tiles of the split and merge, and the decode
+ * body streams with 8 waves. */
 typedef struct ua_plan_info {
     int32_t block_m;       /* query rows per prefill workgroup */
     int32_t block_q;       /* query tokens per prefill workgroup = block_m / (Hq / Hkv) */
     int32_t tile_n;        /* keys per prefill KV tile */
-    int32_t num_waves;     /* 64-lane wavefronts per workgroup (both kernels) */
+    int32_t num_waves;     /* 64-lane wavefronts per workgroup (both bodies): 4, or 8 for split
+                              launches with prefill work (two key groups per query block) */
     int32_t num_splits;    /* splits actually used (1 = no combine launch) */
     int32_t kernels;       /* bit 0: prefill kernel launched; bit 1: decode kernel launched */
     int64_t grid_x;        /* prefill workgroups along (query block slot x kv head); 0 if not launched */

@@ -101,6 +101,7 @@ struct Plan {
     int32_t block_q;       // tokens per prefill workgroup
     int32_t splits;
     int64_t qslots;        // prefill query-block slots
+    bool wide;             // 8-wave workgroups: two prefill key groups per query block
 };
 
 // Kernel choice: every sequence with q_len * G <= kDecodeRows rows goes to the
@@ -143,6 +144,11 @@ Plan make_plan(const ua_attn_params *p) {
             --splits;
     }
     pl.splits = std::max(1, splits);
+    // A split launch with prefill work has few query blocks per kv head (that
+    // is why it splits): its prefill workgroups run two key groups over
+    // alternate tiles, so that one workgroup per CU still puts two waves on
+    // every SIMD.
+    pl.wide = pl.prefill && pl.splits > 1;
     return pl;
 }
 
@@ -261,7 +267,7 @@ ua_status ua_plan(const ua_attn_params *p, ua_plan_info *plan) {
     plan->block_m = ua::kPrefillBlockM;
     plan->block_q = pl.block_q;
     plan->tile_n = ua::kPrefillTileN;
-    plan->num_waves = ua::kWaves;
+    plan->num_waves = pl.wide ? 2 * ua::kWaves : ua::kWaves;
     plan->num_splits = pl.splits;
     plan->kernels = (pl.prefill ? 1 : 0) | (pl.decode ? 2 : 0);
     plan->grid_x = pl.prefill ? pl.qslots * p->num_kv_heads : 0;
@@ -324,7 +330,7 @@ ua_status ua_unified_attention(const ua_attn_params *p, void *stream) {
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool f16 = p->q_dtype == UA_FP16, fp8 = p->kv_dtype == UA_FP8_E4M3FN, causal = p->causal != 0;
-    if (ua::launch_attention(a, f16, fp8, causal, split,
+    if (ua::launch_attention(a, f16, fp8, causal, split, pl.wide,
                              dim3((unsigned)(info.grid_x + info.decode_grid_x), (unsigned)info.grid_y),
                              s) != hipSuccess)
         return UA_ERR_HIP;

@@ -16,11 +16,15 @@
 //     slots from cu[s] / BLOCK_Q + s, and each workgroup finds its sequence by
 //     a binary search over cu_seqlens_q (same section: find_seq_idx and the
 //     slot transform).
+//     Split launches with prefill work (few query blocks per kv head) use
+//     8-wave workgroups instead: two such 4-wave key groups take alternate
+//     tiles of the split, each with its own LDS stages and its own LDS-counter
+//     barrier, and merge their softmax states at the end.
 //   * decode_body: sequences whose q_len * G rows fit one wave (<= 32).
-//     One workgroup per (sequence, kv head, split); its 4 waves hold the same
-//     rows and stream disjoint 32-key units of the key range independently (K
-//     straight into MFMA registers, V through a wave-private LDS stage), then
-//     merge their four partial softmax states at the end.  No barrier in the
+//     One workgroup per (sequence, kv head, split); its 4 (or 8) waves hold
+//     the same rows and stream disjoint 32-key units of the key range
+//     independently (K and V rows loaded whole into wave-private LDS stages),
+//     then merge their partial softmax states at the end.  No barrier in the
 //     key loop, so each wave keeps its own loads in flight.
 //
 // The per-tile step (attend_tile):
@@ -66,11 +70,13 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 // decode merge record per lane: 64 accumulator values, m, l
 constexpr int kDecodeMergeRows = 4 * 16 + 2;
 // LDS of one workgroup of nw waves: the larger of the prefill stages (two K
-// and two V tiles of 64 keys) and the decode merge buffer (nw waves x 66 x 64
-// floats)
+// and two V tiles of 64 keys per 4-wave key group, then two key-group barrier
+// counters) and the merge records (decode: nw waves x 66 x 64 floats; two
+// prefill key groups need 4 waves')
 constexpr int lds_bytes(int nw) {
-    return (2 * 2 * 64 * 256) > (nw * kDecodeMergeRows * 64 * 4) ? (2 * 2 * 64 * 256)
-                                                                  : (nw * kDecodeMergeRows * 64 * 4);
+    return ((nw / 4) * 2 * 2 * 64 * 256 + 16) > (nw * kDecodeMergeRows * 64 * 4)
+               ? ((nw / 4) * 2 * 2 * 64 * 256 + 16)
+               : (nw * kDecodeMergeRows * 64 * 4);
 }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -196,6 +202,27 @@ __device__ __forceinline__ float xhalf_sum(float v) {
 // Wait until every vector-memory load of this wave has completed (including
 // loads that write LDS directly).
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Barrier of the 4 waves of one key group of a two-group prefill workgroup, so
+// that the groups do not run in lock step (one hardware barrier per workgroup
+// would align their MFMA and softmax phases on every SIMD).  One LDS counter
+// per group: a wave adds 1 once its own LDS writes are complete (its direct
+// loads into LDS were waited for before), then polls until the counter reaches
+// target = 4 x (barriers so far).  Every wave of a group passes the same
+// sequence of barriers; the poll count is bounded all the same, so a wave can
+// never spin forever.
+constexpr int kSpinLimit = 1 << 20;
+__device__ __forceinline__ void group_barrier(uint32_t *ctr, uint32_t target, int lane) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (lane == 0)
+        __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    for (int i = 0; i < kSpinLimit; ++i) {
+        if (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target)
+            break;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    asm volatile("" ::: "memory");
+}
 
 // ------------------------------------------------------------------ per-tile step
 
@@ -477,23 +504,42 @@ __device__ __forceinline__ bool locate_block(const AttnArgs &a, int bx, int TN, 
     return true;
 }
 
-// Prefill workgroup bx: 4 waves x 32 rows, 64-key tiles in two LDS stages.
-template <bool F16, bool FP8KV, bool CAUSAL, bool SPLIT>
+// Prefill workgroup bx: KG key groups of 4 waves x 32 rows.  Every group
+// holds all 128 rows; group g takes the tiles t_begin + g, t_begin + g + KG,
+// ... of the block's range through its own two LDS stages, and the groups'
+// softmax states are merged at the end (KG = 2 gives two waves per SIMD where
+// a launch has only about one workgroup per CU).
+template <bool F16, bool FP8KV, bool CAUSAL, bool SPLIT, int KG>
 __device__ __forceinline__ void prefill_body(const AttnArgs &a, int bx, uint8_t *lds) {
     constexpr int NT = 256, TN = 64;
     constexpr int NKB = TN / 32;                // 32-key blocks per tile
     constexpr int KVB = FP8KV ? 1 : 2;          // bytes per cached element
     constexpr int STAGE = 2 * TN * 256;         // bytes of one K + V stage (16-bit in LDS)
-    uint8_t *const sK0 = lds;
-    uint8_t *const sV0 = lds + TN * 256;
-    uint8_t *const sK1 = lds + STAGE;
-    uint8_t *const sV1 = lds + STAGE + TN * 256;
+    static_assert(KG == 1 || KG == 2, "one or two key groups");
+    static_assert(KG * 2 * STAGE + 8 <= lds_bytes(4 * KG) &&
+                      (KG == 1 || 4 * kDecodeMergeRows * 64 * 4 <= KG * 2 * STAGE),
+                  "stages, counters and merge records fit");
 
     const int tid = threadIdx.x;
+    const int grp = KG == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid >> 8);   // key group
+    const int gtid = tid & (NT - 1);            // thread within the group
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = gtid >> 6;                 // row wave within the group
     const int hl = lane >> 5;                   // lane half
     const int lc = lane & 31;                   // accumulator column = query row in the wave
+    uint8_t *const sK0 = lds + grp * (2 * STAGE);
+    uint8_t *const sV0 = sK0 + TN * 256;
+    uint8_t *const sK1 = sK0 + STAGE;
+    uint8_t *const sV1 = sK1 + TN * 256;
+    // key-group barrier counters, after both groups' stages
+    uint32_t *const gctr = (uint32_t *)(lds + KG * 2 * STAGE) + grp;
+    uint32_t n_sync = 0;
+    auto loop_sync = [&]() {
+        if constexpr (KG == 1)
+            __syncthreads();
+        else
+            group_barrier(gctr, 4u * ++n_sync, lane);
+    };
 
     // ---------------------------------------------------------------- tiler
     PrefillBlock B;
@@ -503,6 +549,15 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, int bx, uint8_t 
     const int tq0 = B.tq0, tq1 = B.tq1, kv_len = B.kv_len, ctx = B.ctx, kv_end = B.kv_end;
     const int n_full = B.n_full, t_begin = B.t_begin, t_end = B.t_end;
     const int G = a.group;
+    // iteration k: group g holds tile mine(k) if has(k); barriers follow the
+    // iteration count, which is the same for every group
+    const int n_it = (t_end - t_begin + KG - 1) / KG;
+    auto mine = [&](int k) { return t_begin + grp + KG * k; };
+    auto has = [&](int k) { return mine(k) < t_end; };
+    if constexpr (KG == 2) {
+        if (tid < 2)
+            ((uint32_t *)(lds + KG * 2 * STAGE))[tid] = 0;   // ordered by the first full barrier
+    }
 
     // ---------------------------------------------------------------- rows
     const int r = wave * 32 + lc;
@@ -580,35 +635,38 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, int bx, uint8_t 
                         *(u32x4 *)(sV + (wrow + 4 * i) * 256 + 16 * lane) = u32x4{0, 0, 0, 0};
             }
         };
-        if (t_begin < t_end) {
-            fetch_id(t_begin);
-            dma_tile(t_begin, sK0, sV0);
-            if (t_begin + 1 < t_end)
-                fetch_id(t_begin + 1);
+        if (n_it > 0) {
+            if (has(0)) {
+                fetch_id(mine(0));
+                dma_tile(mine(0), sK0, sV0);
+                if (has(1))
+                    fetch_id(mine(1));
+            }
             wait_vmem();
-            zero_tail(t_begin, sV0);
+            if (has(0))
+                zero_tail(mine(0), sV0);
             __syncthreads();
         }
         // unrolled by two so that each stage's LDS addresses are constants
-        auto step = [&](int tile, uint8_t *cK, uint8_t *cV, uint8_t *nK, uint8_t *nV) {
-            const bool more = tile + 1 < t_end;
-            if (more) {
-                dma_tile(tile + 1, nK, nV);
-                if (tile + 2 < t_end)
-                    fetch_id(tile + 2);
+        auto step = [&](int k, uint8_t *cK, uint8_t *cV, uint8_t *nK, uint8_t *nV) {
+            if (has(k + 1)) {
+                dma_tile(mine(k + 1), nK, nV);
+                if (has(k + 2))
+                    fetch_id(mine(k + 2));
             }
-            if (wave_on)
-                compute(tile, cK, cV);
-            if (more) {
+            if (wave_on && has(k))
+                compute(mine(k), cK, cV);
+            if (k + 1 < n_it) {
                 wait_vmem();
-                zero_tail(tile + 1, nV);
-                __syncthreads();
+                if (has(k + 1))
+                    zero_tail(mine(k + 1), nV);
+                loop_sync();
             }
         };
-        for (int tile = t_begin; tile < t_end; tile += 2) {
-            step(tile, sK0, sV0, sK1, sV1);
-            if (tile + 1 < t_end)
-                step(tile + 1, sK1, sV1, sK0, sV0);
+        for (int k = 0; k < n_it; k += 2) {
+            step(k, sK0, sV0, sK1, sV1);
+            if (k + 1 < n_it)
+                step(k + 1, sK1, sV1, sK0, sV0);
         }
     } else {
         // fp8 caches: codes are loaded into registers two tiles ahead (two
@@ -619,8 +677,8 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, int bx, uint8_t 
         // wave covers an 8-key group (one page), whose id is a scalar load
         // fetched one tile before the loads that use it.
         constexpr int PPT = (TN / 2) * 16 / NT;
-        const int c = tid & 15;
-        const int lanep = 2 * ((tid >> 4) & 3);
+        const int c = gtid & 15;
+        const int lanep = 2 * ((gtid >> 4) & 3);
         const uint32_t lofs0 = (uint32_t)(lanep * a.kv_st_slot + 8 * c) * KVB;
         const uint32_t lofs1 = lofs0 + (uint32_t)a.kv_st_slot * KVB;
         struct Codes {
@@ -657,7 +715,7 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, int bx, uint8_t 
             const bool full = (tile + 1) * TN <= kv_end;
 #pragma unroll
             for (int i = 0; i < PPT; ++i) {
-                const int p = (tid >> 4) + i * (NT / 16);
+                const int p = (gtid >> 4) + i * (NT / 16);
                 const int j0 = 2 * p, j1 = 2 * p + 1;
                 u32x4 k0 = widen_fp8<F16>(r.k[i][0]), k1 = widen_fp8<F16>(r.k[i][1]);
                 u32x4 v0 = widen_fp8<F16>(r.v[i][0]), v1 = widen_fp8<F16>(r.v[i][1]);
@@ -671,55 +729,93 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, int bx, uint8_t 
                 *(u32x4 *)(sV + j1 * 256 + ((c ^ swz_v(j1)) << 4)) = v1;
             }
         };
-        // tile t_begin + k lives in register set R(k % 2) between its load and
-        // its store
-        if (t_begin < t_end) {
-            fetch_ids(t_begin);
-            load_tile(t_begin, R0);
-            if (t_begin + 1 < t_end) {
-                fetch_ids(t_begin + 1);
-                load_tile(t_begin + 1, R1);
+        // the group's k-th tile lives in register set R(k % 2) between its
+        // load and its store
+        if (n_it > 0) {
+            if (has(0)) {
+                fetch_ids(mine(0));
+                load_tile(mine(0), R0);
             }
-            if (t_begin + 2 < t_end)
-                fetch_ids(t_begin + 2);
-            store_tile(t_begin, R0, sK0, sV0);
+            if (has(1)) {
+                fetch_ids(mine(1));
+                load_tile(mine(1), R1);
+            }
+            if (has(2))
+                fetch_ids(mine(2));
+            if (has(0))
+                store_tile(mine(0), R0, sK0, sV0);
             __syncthreads();
-            if (t_begin + 2 < t_end) {
-                load_tile(t_begin + 2, R0);
-                if (t_begin + 3 < t_end)
-                    fetch_ids(t_begin + 3);
+            if (has(2)) {
+                load_tile(mine(2), R0);
+                if (has(3))
+                    fetch_ids(mine(3));
             }
         }
-        // compute(tile) reads one stage while the other receives tile + 1
-        // (from set rn, which then receives tile + 3)
-        auto step = [&](int tile, uint8_t *cK, uint8_t *cV, uint8_t *nK, uint8_t *nV, Codes &rn) {
-            if (wave_on)
-                compute(tile, cK, cV);
-            if (tile + 1 < t_end) {
-                store_tile(tile + 1, rn, nK, nV);
-                __syncthreads();
-                if (tile + 3 < t_end) {
-                    load_tile(tile + 3, rn);
-                    if (tile + 4 < t_end)
-                        fetch_ids(tile + 4);
+        // compute(k) reads one stage while the other receives tile k + 1
+        // (from set rn, which then receives tile k + 3)
+        auto step = [&](int k, uint8_t *cK, uint8_t *cV, uint8_t *nK, uint8_t *nV, Codes &rn) {
+            if (wave_on && has(k))
+                compute(mine(k), cK, cV);
+            if (k + 1 < n_it) {
+                if (has(k + 1))
+                    store_tile(mine(k + 1), rn, nK, nV);
+                loop_sync();
+                if (has(k + 3)) {
+                    load_tile(mine(k + 3), rn);
+                    if (has(k + 4))
+                        fetch_ids(mine(k + 4));
                 }
             }
         };
-        for (int tile = t_begin; tile < t_end; tile += 2) {
-            step(tile, sK0, sV0, sK1, sV1, R1);
-            if (tile + 1 < t_end)
-                step(tile + 1, sK1, sV1, sK0, sV0, R0);
+        for (int k = 0; k < n_it; k += 2) {
+            step(k, sK0, sV0, sK1, sV1, R1);
+            if (k + 1 < n_it)
+                step(k + 1, sK1, sV1, sK0, sV0, R0);
         }
     }
 
     // ---------------------------------------------------------------- epilogue
-    if (!wave_on)
-        return;
-    const float l_row = xhalf_sum(st.l);
-    if (!row_ok)
-        return;
-    write_rows<F16, SPLIT, 4>(a, st.o, 0, st.m, l_row, FP8KV ? *a.v_scale : 1.0f, tok, head, split,
-                              lane, true);
+    if constexpr (KG == 1) {
+        if (!wave_on)
+            return;
+        const float l_row = xhalf_sum(st.l);
+        if (!row_ok)
+            return;
+        write_rows<F16, SPLIT, 4>(a, st.o, 0, st.m, l_row, FP8KV ? *a.v_scale : 1.0f, tok, head,
+                                  split, lane, true);
+    } else {
+        // group 1 leaves (o, m, l) per lane in LDS; group 0 merges them into
+        // its own state (both hold the same rows in the same lanes)
+        const float l_row = xhalf_sum(st.l);
+        __syncthreads();                        // both groups are done with their stages
+        float *rec = (float *)lds + wave * (kDecodeMergeRows * 64);
+        if (grp == 1) {
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    rec[(16 * x + i) * 64 + lane] = st.o[x][i];
+            rec[64 * 64 + lane] = st.m;
+            rec[65 * 64 + lane] = l_row;
+        }
+        __syncthreads();
+        if (grp == 1 || !wave_on)
+            return;
+        const float m1 = rec[64 * 64 + lane];
+        const float M = fmaxf(st.m, m1);
+        const float s0 = (st.m == neg_inf()) ? 0.0f : __builtin_amdgcn_exp2f(st.m - M);
+        const float s1 = (m1 == neg_inf()) ? 0.0f : __builtin_amdgcn_exp2f(m1 - M);
+        const float L = s0 * l_row + s1 * rec[65 * 64 + lane];
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                st.o[x][i] = s0 * st.o[x][i] + s1 * rec[(16 * x + i) * 64 + lane];
+        if (!row_ok)
+            return;
+        write_rows<F16, SPLIT, 4>(a, st.o, 0, M, L, FP8KV ? *a.v_scale : 1.0f, tok, head, split,
+                                  lane, true);
+    }
 }
 
 // ------------------------------------------------------------------ decode kernel
@@ -915,17 +1011,20 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, int bx, uint8_t *
 // the rest the prefill body.  Decode workgroups come first so that, in a
 // mixed batch, their memory-bound streaming shares the CUs with the
 // compute-bound prefill workgroups from the start instead of trailing them.
-// Two workgroups per CU whose waves pair up on each SIMD (wave w of both on
-// SIMD w), so the softmax of one wave overlaps the MFMAs of the other.
-template <bool F16, bool FP8KV, bool CAUSAL, bool SPLIT>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// KG = 1: two 4-wave workgroups per CU whose waves pair up on each SIMD (wave
+// w of both on SIMD w), so the softmax of one wave overlaps the MFMAs of the
+// other.  KG = 2 (split launches with prefill work, which have few query
+// blocks per kv head): one 8-wave workgroup per CU, the prefill body's two key
+// groups (or 8 decode waves) filling the same two slots per SIMD.
+template <bool F16, bool FP8KV, bool CAUSAL, bool SPLIT, int KG>
+__global__ __launch_bounds__(kWaves * KG * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(const AttnArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[lds_bytes(kWaves)];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[lds_bytes(kWaves * KG)];
     const int bx = blockIdx.x;
     if (bx < a.decode_wgs)
-        decode_body<F16, FP8KV, CAUSAL, SPLIT, kWaves>(a, bx, lds);
+        decode_body<F16, FP8KV, CAUSAL, SPLIT, kWaves * KG>(a, bx, lds);
     else
-        prefill_body<F16, FP8KV, CAUSAL, SPLIT>(a, bx - a.decode_wgs, lds);
+        prefill_body<F16, FP8KV, CAUSAL, SPLIT, KG>(a, bx - a.decode_wgs, lds);
 }
 
 // ------------------------------------------------------------------ combine kernel
@@ -985,30 +1084,40 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *o_part, const
 
 // ------------------------------------------------------------------ launchers
 
-template <bool F16, bool FP8KV, bool CAUSAL, bool SPLIT>
+template <bool F16, bool FP8KV, bool CAUSAL, bool SPLIT, int KG>
 hipError_t launch_kernel(const AttnArgs &a, dim3 grid, hipStream_t st) {
-    hipLaunchKernelGGL((attn_fwd_kernel<F16, FP8KV, CAUSAL, SPLIT>), grid, dim3(kWaves * 64), 0, st, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<F16, FP8KV, CAUSAL, SPLIT, KG>), grid, dim3(kWaves * KG * 64), 0,
+                       st, a);
     return hipGetLastError();
 }
 
+// Two key groups only for split launches.
 template <bool F16, bool FP8KV>
-hipError_t launch_mode(const AttnArgs &a, bool causal, bool split, dim3 grid, hipStream_t st) {
-    if (causal)
-        return split ? launch_kernel<F16, FP8KV, true, true>(a, grid, st)
-                     : launch_kernel<F16, FP8KV, true, false>(a, grid, st);
-    return split ? launch_kernel<F16, FP8KV, false, true>(a, grid, st)
-                 : launch_kernel<F16, FP8KV, false, false>(a, grid, st);
+hipError_t launch_mode(const AttnArgs &a, bool causal, bool split, bool wide, dim3 grid,
+                       hipStream_t st) {
+    if (causal) {
+        if (split)
+            return wide ? launch_kernel<F16, FP8KV, true, true, 2>(a, grid, st)
+                        : launch_kernel<F16, FP8KV, true, true, 1>(a, grid, st);
+        return launch_kernel<F16, FP8KV, true, false, 1>(a, grid, st);
+    }
+    if (split)
+        return wide ? launch_kernel<F16, FP8KV, false, true, 2>(a, grid, st)
+                    : launch_kernel<F16, FP8KV, false, true, 1>(a, grid, st);
+    return launch_kernel<F16, FP8KV, false, false, 1>(a, grid, st);
 }
 
 }  // namespace
 
 hipError_t launch_attention(const AttnArgs &a, bool q_f16, bool kv_fp8, bool causal, bool split,
-                            dim3 grid, hipStream_t stream) {
+                            bool wide, dim3 grid, hipStream_t stream) {
+    if (wide && !split)
+        return hipErrorInvalidValue;
     if (q_f16)
-        return kv_fp8 ? launch_mode<true, true>(a, causal, split, grid, stream)
-                      : launch_mode<true, false>(a, causal, split, grid, stream);
-    return kv_fp8 ? launch_mode<false, true>(a, causal, split, grid, stream)
-                  : launch_mode<false, false>(a, causal, split, grid, stream);
+        return kv_fp8 ? launch_mode<true, true>(a, causal, split, wide, grid, stream)
+                      : launch_mode<true, false>(a, causal, split, wide, grid, stream);
+    return kv_fp8 ? launch_mode<false, true>(a, causal, split, wide, grid, stream)
+                  : launch_mode<false, false>(a, causal, split, wide, grid, stream);
 }
 
 hipError_t launch_combine(const float *o_part, const float *lse_part, int32_t num_splits,

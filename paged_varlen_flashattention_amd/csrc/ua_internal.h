@@ -49,9 +49,11 @@ constexpr int kWaves = 4;             // wavefronts per workgroup, both bodies
 
 // Enqueue the attention kernel: grid.x = decode workgroups (S x Hkv) followed
 // by prefill workgroups (slots x Hkv), grid.y = splits.  q_f16: q/out are fp16 (else
-// bf16); kv_fp8: the cache holds fp8 e4m3fn codes (else the q dtype).
+// bf16); kv_fp8: the cache holds fp8 e4m3fn codes (else the q dtype); wide
+// (split launches only): 8-wave workgroups, each prefill workgroup running two
+// key groups over alternate tiles of its split.
 hipError_t launch_attention(const AttnArgs &a, bool q_f16, bool kv_fp8, bool causal, bool split,
-                            dim3 grid, hipStream_t stream);
+                            bool wide, dim3 grid, hipStream_t stream);
 
 // Enqueue the split combine kernel over rows = T * Hq rows.
 hipError_t launch_combine(const float *o_part, const float *lse_part, int32_t num_splits,

@@ -2,6 +2,7 @@
 path through the C ABI, compare with the oracle."""
 from __future__ import annotations
 
+import ctypes
 import os
 import sys
 
@@ -11,6 +12,7 @@ import torch
 import oracle
 import oracle.bruteforce as bf
 import paged_varlen_flashattention_amd as ua
+from paged_varlen_flashattention_amd import _binding as B
 
 TOL = {"bf16": 2e-2, "fp16": 2e-2, "fp8_e4m3fn": 6e-2}
 LSE_TOL = 1e-3
@@ -69,6 +71,21 @@ def run(wl, dev_inputs=None, num_splits=None, want_lse=True, out=None, workspace
     if sync:
         torch.cuda.synchronize()
     return out, lse
+
+
+def plan(wl, num_splits=None):
+    """The launch the library plans for a workload (host only; the workload's
+    CPU tensors stand in for the device buffers and the workspace is unbounded)."""
+    scales = [None if x is None else torch.tensor([x], dtype=torch.float32)
+              for x in (wl.k_scale, wl.v_scale)]
+    p = B.make_params(wl.q, wl.k_cache, wl.v_cache, wl.q, wl.cu_seqlens_q, wl.seqused_k,
+                      wl.block_table, wl.max_seqlen_q, wl.max_seqlen_k, wl.softmax_scale, wl.causal,
+                      *scales, wl.num_splits if num_splits is None else num_splits, None, None)
+    p.workspace, p.workspace_bytes = 256, 1 << 62
+    info = B.PlanInfo()
+    st = B.load_library().ua_plan(ctypes.byref(p), ctypes.byref(info))
+    assert st == B.UA_OK, st
+    return info
 
 
 def out_f64(out: torch.Tensor) -> np.ndarray:

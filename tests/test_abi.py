@@ -113,6 +113,24 @@ def test_plan_gqa_block_q(lib):
     assert info.grid_x == (8256 // 16 + 68) * 8 and info.decode_grid_x == 68 * 8
 
 
+def test_plan_split_prefill_is_wide(lib):
+    # long-context shape (query lens [1, 16], 131072 keys, 64/8 heads, 32
+    # splits): the split launch with prefill work runs 8-wave workgroups; the
+    # same call unsplit, and a decode-only split launch, keep 4 waves
+    shape = dict(num_seqs=2, num_tokens=17, num_q_heads=64, num_kv_heads=8, max_seqlen_q=16,
+                 max_seqlen_k=131072, block_table_stride=8192, num_blocks=16384,
+                 q_stride_token=64 * 128, o_stride_token=64 * 128)
+    need = lib.ua_workspace_size(17, 64, 128, 32)
+    st, info = plan_status(lib, base_params(num_splits=32, workspace=FAKE, workspace_bytes=need,
+                                            **shape))
+    assert st == 0 and info.num_waves == 8 and info.num_splits == 32 and info.kernels == 3
+    st, info = plan_status(lib, base_params(num_splits=1, **shape))
+    assert st == 0 and info.num_waves == 4
+    st, info = plan_status(lib, base_params(num_splits=8, workspace=FAKE,
+                                            workspace_bytes=lib.ua_workspace_size(256, 32, 128, 8)))
+    assert st == 0 and info.num_waves == 4 and info.kernels == 2
+
+
 @pytest.mark.parametrize("field,value,status", [
     ("abi_version", 7, B.UA_ERR_INVALID_ARG),
     ("num_seqs", -1, B.UA_ERR_INVALID_ARG),

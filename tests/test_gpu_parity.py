@@ -133,6 +133,28 @@ def test_split_counts(splits):
     H.compare(wl, out, lse, what=f"splits {splits}")
 
 
+@pytest.mark.parametrize("case", range(8))
+def test_split_prefill_two_key_groups(case):
+    # split launches with prefill work run two 4-wave key groups per workgroup
+    # over alternate tiles of the split: odd and even tile counts per split,
+    # splits with one tile (second group idle) or none, 16-bit and fp8
+    # caches, G = 1, 3, 8, 16
+    heads = [(4, 4), (6, 2), (16, 2), (16, 1)][case % 4]
+    kv_dtype = "fp8_e4m3fn" if case % 2 else None
+    dtype = "fp16" if case in (2, 5) else "bf16"
+    causal = case < 6
+    splits = [2, 3, 7, 5, 4, 9, 2, 3][case]
+    q_lens = [1, 40, 7, 129, 16]
+    kv_lens = [700, 1000, 300, 1500, 64 * 11]
+    wl = wk.make_paged("keygroups", 4200 + case, q_lens, kv_lens, heads[0], heads[1],
+                       block_size=[16, 32][case % 2], dtype=dtype, kv_dtype=kv_dtype, causal=causal)
+    H.say(f"two key groups case={case} heads={heads} splits={splits} kv={kv_dtype} {dtype} causal={causal}")
+    info = H.plan(wl, num_splits=splits)
+    assert info.num_waves == 8
+    out, lse = H.run(wl, num_splits=splits)
+    H.compare(wl, out, lse, what=f"key groups {case}")
+
+
 def test_page_relabel_is_bitwise_invariant():
     wl = wk.make_paged("relabel", 4200, [3, 40, 1], [300, 200, 77], 8, 2, block_size=16, causal=True)
     H.say("page relabel")
