@@ -58,6 +58,10 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
                                   p, p, p, i64, i32, i32, i32, i32, i32, dbl, ctypes.c_int,
                                   dbl, dbl, i32, i32, p, i64, p, p, ctypes.c_int]
     lib.uao_attention.restype = ctypes.c_int
+    lib.uao_attention_ex.argtypes = [p, ctypes.c_int, i64, i64, p, p, ctypes.c_int, i64, i64, i64,
+                                     p, p, p, i64, i32, i32, i32, i32, i32, dbl, ctypes.c_int,
+                                     dbl, dbl, i32, i32, i32, i32, p, p, i64, p, p, ctypes.c_int]
+    lib.uao_attention_ex.restype = ctypes.c_int
     lib.uao_combine.argtypes = [p, p, i32, i64, i32, p, p]
     lib.uao_combine.restype = ctypes.c_int
     lib.uao_decode.argtypes = [ctypes.c_int, p, p, i64]
@@ -95,7 +99,8 @@ def attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
               softmax_scale: float, causal: bool, k_scale: Optional[float] = None,
               v_scale: Optional[float] = None, rows: Optional[np.ndarray] = None,
               kv_range: Optional[Tuple[int, int]] = None, threads: Optional[int] = None,
-              lib: Optional[ctypes.CDLL] = None) -> Tuple[np.ndarray, np.ndarray]:
+              lib: Optional[ctypes.CDLL] = None, window: Tuple[int, int] = (-1, -1),
+              alibi_slopes=None) -> Tuple[np.ndarray, np.ndarray]:
     """fp64 attention over a paged KV cache.
 
     q [T, Hq, D] (bf16/fp16, any token/head strides, unit d stride);
@@ -104,6 +109,9 @@ def attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     rows: optional int array [n, 2] of (token, head); default all rows,
     token-major.  kv_range=(lo, hi) restricts keys to absolute positions
     [lo, hi) (hi < 0: unbounded), which gives one split's partial result.
+    window=(left, right): local attention, keys pos - left .. pos + right of
+    the query at absolute position pos (negative: unbounded); alibi_slopes:
+    [Hq] slopes, logit of key j minus slope[h] * |pos - j| (after the scale).
     Returns out [n, D] (or [T, Hq, D] for all rows) and lse [n] (or [T, Hq]),
     natural log.
     """
@@ -131,14 +139,23 @@ def attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     fp8 = k_cache.dtype == torch.float8_e4m3fn
     if fp8 and (k_scale is None or v_scale is None):
         raise ValueError("fp8 KV needs k_scale and v_scale")
-    rc = lib.uao_attention(
+    if alibi_slopes is not None:
+        alibi = np.ascontiguousarray(np.asarray(
+            alibi_slopes.numpy() if isinstance(alibi_slopes, torch.Tensor) else alibi_slopes,
+            dtype=np.float64).reshape(-1))
+        if alibi.shape[0] != Hq:
+            raise ValueError("alibi_slopes needs one slope per query head")
+    else:
+        alibi = None
+    rc = lib.uao_attention_ex(
         q.data_ptr(), _DTYPE_CODES[q.dtype], q.stride(0), q.stride(1),
         k_cache.data_ptr(), v_cache.data_ptr(), _DTYPE_CODES[k_cache.dtype],
         k_cache.stride(0), k_cache.stride(1), k_cache.stride(2),
         cu.data_ptr(), kv.data_ptr(), bt.data_ptr(), bt.stride(0) if bt.dim() == 2 else 0,
         S, Hq, Hkv, D, bs, float(softmax_scale), int(bool(causal)),
         float(k_scale) if fp8 else 1.0, float(v_scale) if fp8 else 1.0,
-        int(lo), int(hi),
+        int(lo), int(hi), int(window[0]), int(window[1]),
+        alibi.ctypes.data if alibi is not None else None,
         rows_arr.ctypes.data if rows_arr is not None else None, n,
         out.ctypes.data, lse.ctypes.data, int(threads or os.cpu_count() or 1))
     if rc != 0:
@@ -152,7 +169,9 @@ def attention_workload(wl, rows=None, kv_range=None, threads=None, lib=None):
     """attention() on any object with the fields of workloads.Workload."""
     return attention(wl.q, wl.k_cache, wl.v_cache, wl.cu_seqlens_q, wl.seqused_k, wl.block_table,
                      wl.softmax_scale, wl.causal, wl.k_scale, wl.v_scale, rows=rows,
-                     kv_range=kv_range, threads=threads, lib=lib)
+                     kv_range=kv_range, threads=threads, lib=lib,
+                     window=(getattr(wl, "window_left", -1), getattr(wl, "window_right", -1)),
+                     alibi_slopes=getattr(wl, "alibi_slopes", None))
 
 
 def combine(o_part: np.ndarray, lse_part: np.ndarray,

@@ -48,8 +48,12 @@ def to_f64(t: torch.Tensor) -> np.ndarray:
 
 
 def attention(q, k_cache, v_cache, cu_seqlens_q, seqused_k, block_table, softmax_scale,
-              causal, k_scale=None, v_scale=None):
-    """Returns out [T, Hq, D] and lse [T, Hq] (natural log), float64."""
+              causal, k_scale=None, v_scale=None, window=(-1, -1), alibi_slopes=None):
+    """Returns out [T, Hq, D] and lse [T, Hq] (natural log), float64.
+
+    window=(left, right) keeps the band pos - left <= j <= pos + right of the
+    dense score matrix (negative: no bound); alibi_slopes [Hq] adds
+    -slope[h] * |pos - j| to every scaled score."""
     Q = to_f64(q)
     Kc = to_f64(k_cache) * (1.0 if k_scale is None else float(k_scale))
     Vc = to_f64(v_cache) * (1.0 if v_scale is None else float(v_scale))
@@ -73,18 +77,32 @@ def attention(q, k_cache, v_cache, cu_seqlens_q, seqused_k, block_table, softmax
         Vh = np.repeat(Vs, G, axis=1)
         Qs = Q[q0:q1]                          # [ql, Hq, D]
         S_ = np.einsum("ihd,jhd->hij", Qs, Kh) * softmax_scale    # [Hq, ql, kl]
+        pos_q = (kl - ql) + np.arange(ql)[:, None]                # [ql, 1]
+        pos_k = np.arange(kl)[None, :]                            # [1, kl]
+        if alibi_slopes is not None:
+            slopes = np.asarray(alibi_slopes, dtype=np.float64).reshape(-1)
+            S_ = S_ - slopes[:, None, None] * np.abs(pos_q - pos_k)[None]
+        visible = np.ones((ql, kl), dtype=bool)
         if causal:
-            pos_q = (kl - ql) + np.arange(ql)[:, None]
-            visible = np.arange(kl)[None, :] <= pos_q             # [ql, kl]
-            S_ = np.where(visible[None], S_, -np.inf)
+            visible &= pos_k <= pos_q
+        if window[0] >= 0:
+            visible &= pos_k >= pos_q - window[0]
+        if window[1] >= 0:
+            visible &= pos_k <= pos_q + window[1]
+        S_ = np.where(visible[None], S_, -np.inf)
         mx = S_.max(axis=-1, keepdims=True)
-        P = np.exp(S_ - mx)
+        mx_safe = np.where(np.isfinite(mx), mx, 0.0)              # rows with no visible key
+        P = np.exp(S_ - mx_safe)
         den = P.sum(axis=-1, keepdims=True)
-        out[q0:q1] = np.einsum("hij,jhd->ihd", P / den, Vh)
-        lse[q0:q1] = (mx + np.log(den))[..., 0].T
+        W = np.divide(P, den, out=np.zeros_like(P), where=den > 0)
+        out[q0:q1] = np.einsum("hij,jhd->ihd", W, Vh)
+        lse[q0:q1] = np.where(den > 0, mx_safe + np.log(np.where(den > 0, den, 1.0)), -np.inf)[..., 0].T
     return out, lse
 
 
 def attention_workload(wl):
+    slopes = getattr(wl, "alibi_slopes", None)
     return attention(wl.q, wl.k_cache, wl.v_cache, wl.cu_seqlens_q, wl.seqused_k, wl.block_table,
-                     wl.softmax_scale, wl.causal, wl.k_scale, wl.v_scale)
+                     wl.softmax_scale, wl.causal, wl.k_scale, wl.v_scale,
+                     window=(getattr(wl, "window_left", -1), getattr(wl, "window_right", -1)),
+                     alibi_slopes=None if slopes is None else to_f64(slopes))

@@ -24,7 +24,15 @@
  *     kv_len - q_len + i and sees keys 0 .. kv_len - q_len + i (same section:
  *     context_len is the number of tokens before the current queries);
  *   - fp8 KV values dequantised as code * scale (same section: K and V are
- *     loaded, then dequantised with their per-tensor scales).
+ *     loaded, then dequantised with their per-tensor scales);
+ *   - optional local (sliding-window) attention and ALiBi bias, the two
+ *     switches of the FA2 forward launch (page "flashatten takeaways EP2 工程",
+ *     section "源代码接口": window_size_left / window_size_right and
+ *     alibi_slopes_ptr).  The pages name the switches but not their formulas;
+ *     the reading taken here is the usual one: with the query at absolute
+ *     position pos, keys pos - window_left .. pos + window_right are visible (a
+ *     negative bound is no bound), and the logit of key j gets
+ *     -slope[h] * |pos - j| added after the softmax scale.
  * It is computed in double precision, with exp/log from libm, summed in
  * key order.  No blocking, no online rescaling, no split.
  *
@@ -115,6 +123,8 @@ typedef struct {
     int32_t num_seqs, num_q_heads, num_kv_heads, head_size, block_size;
     double scale; int causal; double k_scale, v_scale;
     int32_t kv_lo, kv_hi;
+    int32_t win_left, win_right;                  /* < 0: no bound on that side */
+    const double *alibi;                          /* [num_q_heads] slopes, or NULL */
 } problem;
 
 /* Element offset of (logical key position pos, kv head g, dim d) of sequence s. */
@@ -147,9 +157,14 @@ static void one_row(const problem *p, int64_t t, int32_t h, double *out, double 
 
     /* visible keys: [0, kv_len), and j <= ctx + i when causal, intersected with
        [kv_lo, kv_hi) when a partial result over a key range is asked for */
+    const int32_t pos = ctx + i;                  /* absolute position of the query */
     int32_t lo = 0, hi = kv_len;
     if (p->causal && ctx + i + 1 < hi)
         hi = ctx + i + 1;
+    if (p->win_left >= 0 && pos - p->win_left > lo)
+        lo = pos - p->win_left;
+    if (p->win_right >= 0 && pos + p->win_right + 1 < hi)
+        hi = pos + p->win_right + 1;
     if (p->kv_lo > lo)
         lo = p->kv_lo;
     if (p->kv_hi >= 0 && p->kv_hi < hi)
@@ -169,6 +184,8 @@ static void one_row(const problem *p, int64_t t, int32_t h, double *out, double 
         for (int32_t d = 0; d < D; ++d)
             dot += qv[d] * (load(p->k, p->kv_dtype, kv_offset(p, s, j, g, d)) * p->k_scale);
         z[j - lo] = p->scale * dot;
+        if (p->alibi)
+            z[j - lo] -= p->alibi[h] * fabs((double)(pos - j));
         if (z[j - lo] > m)
             m = z[j - lo];
     }
@@ -194,8 +211,44 @@ static void one_row(const problem *p, int64_t t, int32_t h, double *out, double 
  * lse is [n_rows] (natural log of the softmax denominator, max included).
  * kv_lo / kv_hi (kv_hi < 0: no upper bound) restrict the keys to a range of
  * absolute positions, which yields the partial result of one split.
+ * win_left / win_right (< 0: unbounded) give local attention, alibi_slopes
+ * ([num_q_heads] or NULL) the ALiBi bias (see the header).
  * Returns 0, or -1 on an invalid argument.
  */
+int uao_attention_ex(const void *q, int q_dtype, int64_t q_st_tok, int64_t q_st_head,
+                     const void *k_cache, const void *v_cache, int kv_dtype,
+                     int64_t kv_st_blk, int64_t kv_st_slot, int64_t kv_st_head,
+                     const int32_t *cu_seqlens_q, const int32_t *seqused_k,
+                     const int32_t *block_table, int64_t bt_stride,
+                     int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                     int32_t head_size, int32_t block_size,
+                     double softmax_scale, int causal, double k_scale, double v_scale,
+                     int32_t kv_lo, int32_t kv_hi,
+                     int32_t win_left, int32_t win_right, const double *alibi_slopes,
+                     const int64_t *rows, int64_t n_rows,
+                     double *out, double *lse, int nthreads)
+{
+    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_size <= 0 || block_size <= 0)
+        return -1;
+    if (num_q_heads % num_kv_heads != 0)
+        return -1;
+    problem p = {q, q_dtype, q_st_tok, q_st_head, k_cache, v_cache, kv_dtype,
+                 kv_st_blk, kv_st_slot, kv_st_head, cu_seqlens_q, seqused_k, block_table, bt_stride,
+                 num_seqs, num_q_heads, num_kv_heads, head_size, block_size,
+                 softmax_scale, causal, k_scale, v_scale, kv_lo, kv_hi,
+                 win_left, win_right, alibi_slopes};
+    if (nthreads < 1)
+        nthreads = 1;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+    for (int64_t r = 0; r < n_rows; ++r) {
+        int64_t t = rows ? rows[2 * r] : r / num_q_heads;
+        int32_t h = (int32_t)(rows ? rows[2 * r + 1] : r % num_q_heads);
+        one_row(&p, t, h, out + r * head_size, lse + r);
+    }
+    return 0;
+}
+
+/* uao_attention_ex without local attention or ALiBi. */
 int uao_attention(const void *q, int q_dtype, int64_t q_st_tok, int64_t q_st_head,
                   const void *k_cache, const void *v_cache, int kv_dtype,
                   int64_t kv_st_blk, int64_t kv_st_slot, int64_t kv_st_head,
@@ -208,23 +261,11 @@ int uao_attention(const void *q, int q_dtype, int64_t q_st_tok, int64_t q_st_hea
                   const int64_t *rows, int64_t n_rows,
                   double *out, double *lse, int nthreads)
 {
-    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_size <= 0 || block_size <= 0)
-        return -1;
-    if (num_q_heads % num_kv_heads != 0)
-        return -1;
-    problem p = {q, q_dtype, q_st_tok, q_st_head, k_cache, v_cache, kv_dtype,
-                 kv_st_blk, kv_st_slot, kv_st_head, cu_seqlens_q, seqused_k, block_table, bt_stride,
-                 num_seqs, num_q_heads, num_kv_heads, head_size, block_size,
-                 softmax_scale, causal, k_scale, v_scale, kv_lo, kv_hi};
-    if (nthreads < 1)
-        nthreads = 1;
-#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
-    for (int64_t r = 0; r < n_rows; ++r) {
-        int64_t t = rows ? rows[2 * r] : r / num_q_heads;
-        int32_t h = (int32_t)(rows ? rows[2 * r + 1] : r % num_q_heads);
-        one_row(&p, t, h, out + r * head_size, lse + r);
-    }
-    return 0;
+    return uao_attention_ex(q, q_dtype, q_st_tok, q_st_head, k_cache, v_cache, kv_dtype,
+                            kv_st_blk, kv_st_slot, kv_st_head, cu_seqlens_q, seqused_k,
+                            block_table, bt_stride, num_seqs, num_q_heads, num_kv_heads,
+                            head_size, block_size, softmax_scale, causal, k_scale, v_scale,
+                            kv_lo, kv_hi, -1, -1, NULL, rows, n_rows, out, lse, nthreads);
 }
 
 /*

@@ -19,7 +19,14 @@ What pins what:
     the mean of the visible values; relabelling physical pages changes nothing;
     replicating kv heads for every query head changes nothing; a one-hot value
     code returns the softmax weights; partial results over any split of the keys
-    merge back into the whole.
+    merge back into the whole;
+  * local attention and ALiBi (the FA2 window / slope switches): a (0, 0)
+    window returns the value at the query's own position exactly; with zero
+    keys and one-hot values the ALiBi weights are r^|pos - j| normalised, whose
+    sum is a closed-form geometric series (the sign, the absolute value, the
+    bottom-right position and the per-head slope all show); zero slopes and a
+    window wider than the sequence change no bit; and the numpy brute force on
+    tiny batches with random windows and slopes.
 """
 from __future__ import annotations
 
@@ -355,11 +362,120 @@ def check_page_structure():
     assert math.ceil(g["config1_longest_kv"] / g["config1_block_size"]) == g["config1_block_table_shape"][1]
 
 
+# ----------------------------------------------------------------- local attention and ALiBi
+
+def _value_lookup(wl, s, j, g):
+    """Decoded (and scaled) value row of key j, kv head g, sequence s."""
+    V = bf.to_f64(wl.v_cache) * (1.0 if wl.v_scale is None else wl.v_scale)
+    bt = wl.block_table.numpy()
+    bs = wl.block_size
+    return V[bt[s, j // bs], j % bs, g]
+
+
+def check_window_own_key(lib):
+    """Window (0, 0), not causal: each query sees only the key at its own
+    absolute position kv_len - q_len + i, so the output is that value row
+    exactly; with q = 0 the one score is 0 and lse = 0."""
+    for kv_dtype in (None, "fp8_e4m3fn"):
+        wl = wk.make_paged("win_own", 2501, [2, 1, 5], [9, 30, 17], 4, 2, block_size=16,
+                           causal=False, kv_dtype=kv_dtype)
+        wl = wk.with_mask(wl, 0, 0)
+        out, lse = oracle.attention_workload(wl, lib=lib)
+        cu = wl.cu_seqlens_q.tolist()
+        for s, kl in enumerate(wl.kv_lens.tolist()):
+            ql = cu[s + 1] - cu[s]
+            for i in range(ql):
+                for h in range(4):
+                    want = _value_lookup(wl, s, kl - ql + i, h // 2)
+                    assert np.array_equal(out[cu[s] + i, h], want), "(0, 0) window returns v_pos"
+        wl.q.zero_()
+        _, lse0 = oracle.attention_workload(wl, lib=lib)
+        assert np.array_equal(lse0, np.zeros_like(lse0)), "one zero score: lse = 0"
+
+
+def _geometric(r, n):
+    """sum_{d=0}^{n-1} r^d in closed form."""
+    return n if r == 1.0 else (1.0 - r ** n) / (1.0 - r)
+
+
+def check_alibi_geometric(lib):
+    """Zero keys, one-hot values (key j -> e_j): the scores are the ALiBi bias
+    alone, so out[j] = r^|pos - j| / Z with r = exp(-slope) and Z a geometric
+    sum in closed form; lse = ln Z.  Causal (with and without a left window)
+    and full, per-head slopes through GQA."""
+    slopes = np.array([0.5, 0.25, 0.125, 0.0625, 1.5, 0.03125], dtype=np.float64)
+    for causal, window in ((True, (-1, -1)), (True, (6, -1)), (False, (-1, -1)), (False, (4, 3))):
+        wl = wk.make_paged("alibi_geo", 2601, [3, 1, 4], [20, 37, 9], 6, 2, block_size=16,
+                           causal=causal)
+        wl.k_cache.zero_()
+        wl.v_cache.zero_()
+        bt = wl.block_table.numpy()
+        for s, kl in enumerate(wl.kv_lens.tolist()):
+            for j in range(kl):
+                wl.v_cache[bt[s, j // 16], j % 16, :, j] = 1.0
+        wl = wk.with_mask(wl, window[0], window[1], torch.tensor(slopes, dtype=torch.float32))
+        out, lse = oracle.attention_workload(wl, lib=lib)
+        cu = wl.cu_seqlens_q.tolist()
+        for s, kl in enumerate(wl.kv_lens.tolist()):
+            ql = cu[s + 1] - cu[s]
+            for i in range(ql):
+                pos = kl - ql + i
+                lo = max(0, pos - window[0]) if window[0] >= 0 else 0
+                hi = min(kl - 1, pos + window[1]) if window[1] >= 0 else kl - 1
+                if causal:
+                    hi = min(hi, pos)
+                for h in range(6):
+                    r = math.exp(-float(np.float32(slopes[h])))
+                    Z = _geometric(r, pos - lo + 1) + r * _geometric(r, hi - pos)
+                    t = cu[s] + i
+                    _close(lse[t, h], math.log(Z), tol=1e-12, what="alibi lse geometric")
+                    want = np.zeros(wl.head_size)
+                    for j in range(lo, hi + 1):
+                        want[j] = r ** abs(pos - j) / Z
+                    _close(out[t, h], want, tol=1e-12, what="alibi weights")
+
+
+def check_mask_neutral_settings(lib):
+    """Zero slopes and a window wider than every sequence change no bit."""
+    wl = wk.make_paged("neutral", 2701, [1, 6, 3], [40, 6, 25], 4, 1, block_size=16, causal=True)
+    base, lbase = oracle.attention_workload(wl, lib=lib)
+    for w in (wk.with_mask(wl, alibi=torch.zeros(4)), wk.with_mask(wl, 10_000, 10_000)):
+        out, lse = oracle.attention_workload(w, lib=lib)
+        assert np.array_equal(out, base) and np.array_equal(lse, lbase), "neutral mask settings"
+
+
+def check_mask_bruteforce(lib, n: int = 30):
+    """Random windows, slopes, causal flags and GQA on tiny batches against the
+    numpy brute force (dense band masks, an independent formulation)."""
+    rng = np.random.default_rng(2801)
+    for c in range(n):
+        S = int(rng.integers(1, 4))
+        kv = [int(rng.integers(1, 70)) for _ in range(S)]
+        ql = [int(rng.integers(0, k + 1)) for k in kv]
+        Hkv = int(rng.choice([1, 2]))
+        Hq = Hkv * int(rng.choice([1, 2, 3]))
+        wl = wk.make_paged("mask_bf", 2810 + c, ql, kv, Hq, Hkv, block_size=16,
+                           causal=bool(rng.integers(0, 2)),
+                           kv_dtype="fp8_e4m3fn" if c % 5 == 4 else None)
+        left = int(rng.choice([-1, 0, 1, 5, 17]))
+        right = int(rng.choice([-1, 0, 2, 9]))
+        slopes = torch.tensor(rng.uniform(0.0, 1.0, Hq), dtype=torch.float32) if c % 2 else None
+        wl = wk.with_mask(wl, left, right, slopes)
+        a, la = oracle.attention_workload(wl, lib=lib)
+        b, lb = bf.attention_workload(wl)
+        _close(a, b, tol=1e-12, what=f"mask brute force case {c}")
+        assert np.array_equal(np.isneginf(la), np.isneginf(lb)), "empty rows agree"
+        fin = np.isfinite(lb)
+        _close(la[fin], lb[fin], tol=1e-12, what=f"mask brute force lse case {c}")
+
+
 QUICK_BATTERY = [
     check_golden_attention, check_golden_combine, check_decoders, check_single_key,
     check_equal_keys, check_page_relabel, check_gqa_replication, check_value_codes,
     check_split_algebra, check_sdpa,
     lambda lib: check_bruteforce(lib, n=25),
+    check_window_own_key, check_alibi_geometric, check_mask_neutral_settings,
+    lambda lib: check_mask_bruteforce(lib, n=12),
 ]
 
 

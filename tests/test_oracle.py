@@ -65,3 +65,19 @@ def test_split_algebra(lib):
 
 def test_page_structure():
     pins.check_page_structure()
+
+
+def test_window_own_key(lib):
+    pins.check_window_own_key(lib)
+
+
+def test_alibi_geometric(lib):
+    pins.check_alibi_geometric(lib)
+
+
+def test_mask_neutral_settings(lib):
+    pins.check_mask_neutral_settings(lib)
+
+
+def test_mask_bruteforce(lib):
+    pins.check_mask_bruteforce(lib, n=40)

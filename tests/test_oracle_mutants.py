@@ -40,6 +40,16 @@ MUTANTS = {
     "combine_lse_without_max": ("lse[r] = L + log(wsum);", "lse[r] = log(wsum);"),
     "combine_no_normalise":   ("out[r * head_size + d] /= wsum;", "out[r * head_size + d] /= 1.0;"),
     "kv_range_ignored":       ("if (p->kv_hi >= 0 && p->kv_hi < hi)", "if (0)"),
+    "window_left_off_by_one": ("lo = pos - p->win_left;", "lo = pos - p->win_left + 1;"),
+    "window_left_ignored":    ("if (p->win_left >= 0 && pos - p->win_left > lo)", "if (0)"),
+    "window_right_off_by_one": ("hi = pos + p->win_right + 1;", "hi = pos + p->win_right;"),
+    "window_right_ignored":   ("if (p->win_right >= 0 && pos + p->win_right + 1 < hi)", "if (0)"),
+    "alibi_sign":             ("z[j - lo] -= p->alibi[h]", "z[j - lo] += p->alibi[h]"),
+    "alibi_from_context_start": ("fabs((double)(pos - j))", "fabs((double)(ctx - j))"),
+    "alibi_without_abs":      ("fabs((double)(pos - j))", "((double)(pos - j))"),
+    "alibi_kv_head_slope":    ("p->alibi[h] *", "p->alibi[g] *"),
+    "alibi_before_scale":     ("z[j - lo] = p->scale * dot;\n        if (p->alibi)\n            z[j - lo] -= p->alibi[h] * fabs((double)(pos - j));",
+                               "z[j - lo] = dot;\n        if (p->alibi)\n            z[j - lo] -= p->alibi[h] * fabs((double)(pos - j));\n        z[j - lo] *= p->scale;"),
 }
 
 

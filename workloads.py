@@ -61,6 +61,9 @@ class Workload:
     v_scale: Optional[float] = None
     num_splits: int = 1
     meta: dict = field(default_factory=dict)
+    window_left: int = -1            # local attention: keys pos - left .. pos + right (-1: unbounded)
+    window_right: int = -1
+    alibi_slopes: Optional[torch.Tensor] = None   # [Hq] fp32 ALiBi slopes, or None
 
     @property
     def q_lens(self) -> np.ndarray:
@@ -108,10 +111,21 @@ class Workload:
         return int(self.kv_lens.max()) if self.num_seqs else 0
 
     def visible_pairs(self) -> int:
-        """Number of visible (query, key) pairs per query head (causal: bottom-right aligned)."""
+        """Number of visible (query, key) pairs per query head (causal: bottom-right
+        aligned; with a window, only keys pos - left .. pos + right)."""
         total = 0
+        local = self.window_left >= 0 or self.window_right >= 0
         for ql, kl in zip(self.q_lens.tolist(), self.kv_lens.tolist()):
-            if self.causal:
+            if local:
+                pos = np.arange(kl - ql, kl, dtype=np.int64)
+                lo = np.maximum(pos - self.window_left, 0) if self.window_left >= 0 else np.zeros_like(pos)
+                hi = np.full_like(pos, kl)
+                if self.causal:
+                    hi = np.minimum(hi, pos + 1)
+                if self.window_right >= 0:
+                    hi = np.minimum(hi, pos + self.window_right + 1)
+                total += int(np.maximum(hi - lo, 0).sum())
+            elif self.causal:
                 ctx = kl - ql
                 # query i sees keys 0 .. ctx + i
                 total += ql * ctx + ql * (ql + 1) // 2
@@ -278,6 +292,28 @@ def make_paged(name: str, seed_id: int, q_lens: Sequence[int], kv_lens: Sequence
         causal=causal, k_scale=k_scale, v_scale=v_scale, num_splits=num_splits,
         meta={"seed_id": seed_id, "table_mode": table_mode, "dtype": dtype, "kv_dtype": kv_dtype},
     )
+
+
+def alibi_slopes(num_heads: int) -> torch.Tensor:
+    """The customary ALiBi slopes for num_heads heads: the geometric sequence
+    2^(-8 (h + 1) / n) for the next power of two n >= num_heads, interleaved as
+    usual when num_heads is not a power of two.  fp32 [num_heads]."""
+    def pow2(n):
+        return [2.0 ** (-8.0 * (h + 1) / n) for h in range(n)]
+    n = 1 << (max(num_heads, 1) - 1).bit_length()
+    if n == num_heads:
+        vals = pow2(n)
+    else:
+        half = n // 2
+        vals = pow2(half) + pow2(n)[0::2][: num_heads - half]
+    return torch.tensor(vals, dtype=torch.float32)
+
+
+def with_mask(wl: Workload, window_left: int = -1, window_right: int = -1,
+              alibi: Optional[torch.Tensor] = None, name: Optional[str] = None) -> Workload:
+    """The same batch with local attention and / or ALiBi slopes."""
+    return Workload(**{**wl.__dict__, "name": name or wl.name, "window_left": int(window_left),
+                       "window_right": int(window_right), "alibi_slopes": alibi})
 
 
 def config1() -> Workload:
