@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define UA_ABI_VERSION 1u
+#define UA_ABI_VERSION 2u
 
 typedef enum {
     UA_OK = 0,
@@ -90,6 +90,17 @@ typedef enum {
  * causal       0: every query sees keys [0, kv_len).  1: query i of sequence
  *              s sits at position kv_len - q_len + i and sees keys
  *              [0, kv_len - q_len + i] (queries are the newest tokens).
+ * window_left, local attention (the window switches of the FA2 forward launch,
+ * window_right page "flashatten takeaways EP2 工程", section "源代码接口"): the
+ *              query at position pos = kv_len - q_len + i also needs
+ *              pos - window_left <= j (window_left >= 0) and
+ *              j <= pos + window_right (window_right >= 0); -1 = no bound on
+ *              that side.  Combined with causal, causal is the tighter right
+ *              bound.
+ * alibi_slopes optional [Hq] device fp32 (4-byte aligned), or NULL: ALiBi (the
+ *              same launch's alibi_slopes_ptr switch).  The logit of key j for
+ *              query head h is softmax_scale * q . k_j - alibi_slopes[h] *
+ *              |pos - j|.  Positions must stay below 2^24 (exact in fp32).
  * k_scale,     device fp32 scalars, required iff kv_dtype is fp8 (else NULL):
  * v_scale      a stored code c means the value c * scale.
  * num_splits   0 = choose automatically, 1 = no split, 2..128 = split each
@@ -140,6 +151,9 @@ typedef struct ua_attn_params {
     int32_t max_seqlen_q, max_seqlen_k;
     int32_t num_splits;
     float softmax_scale;
+    int32_t window_left;             /* -1 = unbounded */
+    int32_t window_right;            /* -1 = unbounded */
+    const float *alibi_slopes;       /* [Hq] or NULL */
 } ua_attn_params;
 
 /* The launch the library chose for a call (filled by ua_plan).  Two kernels

@@ -15,7 +15,7 @@ import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libua.so")
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 UA_OK, UA_ERR_INVALID_ARG, UA_ERR_UNSUPPORTED, UA_ERR_WORKSPACE, UA_ERR_HIP = 0, -1, -2, -3, -4
 UA_BF16, UA_FP16, UA_FP8_E4M3FN = 0, 1, 2
@@ -53,6 +53,8 @@ class AttnParams(ctypes.Structure):
         ("num_blocks", ctypes.c_int32), ("block_table_stride", ctypes.c_int32),
         ("max_seqlen_q", ctypes.c_int32), ("max_seqlen_k", ctypes.c_int32),
         ("num_splits", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+        ("window_left", ctypes.c_int32), ("window_right", ctypes.c_int32),
+        ("alibi_slopes", ctypes.c_void_p),
     ]
 
 
@@ -152,7 +154,7 @@ def workspace_size(num_tokens: int, num_q_heads: int, head_size: int, num_splits
 
 def make_params(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table, max_seqlen_q,
                 max_seqlen_k, softmax_scale, causal, k_scale=None, v_scale=None, num_splits=1,
-                lse=None, workspace=None) -> AttnParams:
+                lse=None, workspace=None, window=(-1, -1), alibi_slopes=None) -> AttnParams:
     """Fill ua_attn_params from tensors (no copies, no device work)."""
     p = AttnParams()
     p.abi_version = ABI_VERSION
@@ -184,6 +186,11 @@ def make_params(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table, 
     p.max_seqlen_k = int(max_seqlen_k)
     p.num_splits = int(num_splits)
     p.softmax_scale = float(softmax_scale)
+    p.window_left, p.window_right = int(window[0]), int(window[1])
+    if alibi_slopes is not None and (alibi_slopes.dtype != torch.float32 or
+                                     alibi_slopes.numel() != q.shape[1]):
+        raise ValueError("alibi_slopes must be fp32 with one slope per query head")
+    p.alibi_slopes = _ptr(alibi_slopes)
     return p
 
 
@@ -197,25 +204,29 @@ def plan(params: AttnParams) -> dict:
 
 
 def auto_splits(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table, max_seqlen_q,
-                max_seqlen_k, softmax_scale, causal, k_scale=None, v_scale=None) -> int:
+                max_seqlen_k, softmax_scale, causal, k_scale=None, v_scale=None, window=(-1, -1),
+                alibi_slopes=None) -> int:
     """The split count the planner picks for num_splits = 0 given unlimited
     workspace (host only, no device work)."""
     probe = make_params(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table,
                         max_seqlen_q, max_seqlen_k, softmax_scale, causal, k_scale, v_scale, 0,
-                        None, None)
+                        None, None, window, alibi_slopes)
     probe.workspace, probe.workspace_bytes = 256, 1 << 62
     return plan(probe)["num_splits"]
 
 
 def unified_attention(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table,
                       max_seqlen_q, max_seqlen_k, softmax_scale, causal, k_scale=None,
-                      v_scale=None, num_splits=1, lse=None, workspace=None, stream=None):
+                      v_scale=None, num_splits=1, lse=None, workspace=None, stream=None,
+                      window=(-1, -1), alibi_slopes=None):
     """ua_unified_attention on torch device tensors; writes `out` (and `lse`).
 
     q [T, Hq, 128] bf16/fp16; k_cache, v_cache [NB, bs, Hkv, 128] (q dtype or
     float8_e4m3fn); out like q; cu_seqlens_q [S+1] int32; seqused_k [S] int32;
     block_table [S, W] int32; k_scale / v_scale 1-element fp32 device tensors for
-    fp8 caches; lse optional [T, Hq] fp32.  With num_splits > 1 (or 0 = auto) a
+    fp8 caches; lse optional [T, Hq] fp32; window (left, right) local attention
+    bounds (-1 = unbounded); alibi_slopes optional [Hq] fp32 device tensor.
+    With num_splits > 1 (or 0 = auto) a
     workspace of workspace_size(...) bytes is allocated here when none is
     given.  Enqueued on `stream` (default: torch's current stream).
     """
@@ -224,12 +235,13 @@ def unified_attention(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_t
         if splits == 0:
             splits = auto_splits(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table,
                                  max_seqlen_q, max_seqlen_k, softmax_scale, causal, k_scale,
-                                 v_scale)
+                                 v_scale, window, alibi_slopes)
         nbytes = workspace_size(q.shape[0], q.shape[1], q.shape[2], splits)
         if nbytes:
             workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     p = make_params(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table, max_seqlen_q,
-                    max_seqlen_k, softmax_scale, causal, k_scale, v_scale, num_splits, lse, workspace)
+                    max_seqlen_k, softmax_scale, causal, k_scale, v_scale, num_splits, lse, workspace,
+                    window, alibi_slopes)
     st = load_library().ua_unified_attention(ctypes.byref(p), _stream_handle(stream))
     if st != UA_OK:
         raise UAError(st, "ua_unified_attention")

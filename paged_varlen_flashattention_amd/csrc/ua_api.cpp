@@ -74,6 +74,10 @@ ua_status validate(const ua_attn_params *p) {
         return UA_ERR_INVALID_ARG;
     if (p->causal != 0 && p->causal != 1)
         return UA_ERR_INVALID_ARG;
+    if (p->window_left < -1 || p->window_right < -1 || !aligned(p->alibi_slopes, 4))
+        return UA_ERR_INVALID_ARG;
+    if (p->alibi_slopes && p->max_seqlen_k > (1 << 24))
+        return UA_ERR_UNSUPPORTED;                             // positions exact in fp32
     if (!p->q || !p->k_cache || !p->v_cache || !p->out || !p->cu_seqlens_q || !p->seqused_k ||
         !p->block_table)
         return UA_ERR_INVALID_ARG;
@@ -327,6 +331,9 @@ ua_status ua_unified_attention(const ua_attn_params *p, void *stream) {
     a.scale_log2 = p->softmax_scale * 1.44269504088896341f;
 
     a.decode_wgs = (int32_t)info.decode_grid_x;
+    a.win_left = p->window_left;
+    a.win_right = p->window_right;
+    a.alibi = p->alibi_slopes;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool f16 = p->q_dtype == UA_FP16, fp8 = p->kv_dtype == UA_FP8_E4M3FN, causal = p->causal != 0;

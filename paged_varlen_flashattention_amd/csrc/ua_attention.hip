@@ -270,11 +270,24 @@ __device__ __forceinline__ void tile_scores(f32x16 (&sacc)[NKB], const u32x4 (&q
     __builtin_amdgcn_s_setprio(0);
 }
 
+// Per-row extras of the local-attention / ALiBi path (page "flashatten
+// takeaways EP2 工程", section "源代码接口": the window and ALiBi switches of the
+// FA2 forward launch): the first visible key (keys below it are masked like
+// those at or past lim) and the ALiBi term -slope * |pos - j| in log2 units.
+struct RowExt {
+    int lo;        // first visible key of the row
+    int pos;       // absolute position of the row's query (below 2^24: exact in fp32)
+    float sl2;     // ALiBi slope * log2(e) (0 without ALiBi)
+};
+
 // Mask, row max, (lazy) rescale of the state, weights and their row sum; the
-// weights leave as the 16-bit B operand pf of O^T += V^T P^T.
-template <bool F16, int NKB>
+// weights leave as the 16-bit B operand pf of O^T += V^T P^T.  EXT: also the
+// lower bound of a local window and, when alibi, the ALiBi term (added to the
+// scaled score before the row max).
+template <bool F16, int NKB, bool EXT = false>
 __device__ __forceinline__ void tile_softmax(RowState &st, f32x16 (&sacc)[NKB], u32x4 (&pf)[2 * NKB],
-                                             int key0, bool masked, int lim, float c2, int lane) {
+                                             int key0, bool masked, int lim, float c2, int lane,
+                                             RowExt ext = RowExt{0, 0, 0.0f}, bool alibi = false) {
     const int hl = lane >> 5;
     // mask (boundary / diagonal tiles only) and row max
     if (masked) {
@@ -284,9 +297,27 @@ __device__ __forceinline__ void tile_softmax(RowState &st, f32x16 (&sacc)[NKB], 
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
                 const int j = j0 + 32 * b + 16 * (q >> 3) + (q & 7);
-                if (j >= lim)
+                if (j >= lim || (EXT && j < ext.lo))
                     sacc[b][q] = neg_inf();
             }
+    }
+    if constexpr (EXT) {
+        if (alibi) {                            // uniform: the launch has slopes
+            // scaled score with the bias, in log2 units; the rest then runs
+            // with a unit scale
+            const int base = ext.pos - (key0 + 8 * hl);
+            const float nsl2 = -ext.sl2;
+#pragma unroll
+            for (int b = 0; b < NKB; ++b)
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const int d = base - (32 * b + 16 * (q >> 3) + (q & 7));
+                    sacc[b][q] = __builtin_fmaf(nsl2, __builtin_fabsf((float)d), sacc[b][q] * c2);
+                    if ((q & 3) == 3)
+                        __builtin_amdgcn_sched_barrier(0);   // keep the temporaries few
+                }
+            c2 = 1.0f;
+        }
     }
     float mx = neg_inf();
 #pragma unroll
@@ -367,13 +398,14 @@ __device__ __forceinline__ void tile_pv(RowState &st, const u32x4 (&pf)[2 * NKB]
             st.o[x] = mfma32<F16>(vfrag(kk, x), pf[kk], st.o[x]);
 }
 
-template <bool F16, int NKB, class KF, class VF>
+template <bool F16, int NKB, bool EXT = false, class KF, class VF>
 __device__ __forceinline__ void attend_tile(RowState &st, const u32x4 (&qf)[8], KF kfrag, VF vfrag,
-                                            int key0, bool masked, int lim, float c2, int lane) {
+                                            int key0, bool masked, int lim, float c2, int lane,
+                                            RowExt ext = RowExt{0, 0, 0.0f}, bool alibi = false) {
     f32x16 sacc[NKB];
     u32x4 pf[2 * NKB];
     tile_scores<F16, NKB>(sacc, qf, kfrag);
-    tile_softmax<F16, NKB>(st, sacc, pf, key0, masked, lim, c2, lane);
+    tile_softmax<F16, NKB, EXT>(st, sacc, pf, key0, masked, lim, c2, lane, ext, alibi);
     tile_pv<F16, NKB>(st, pf, vfrag);
 }
 
@@ -460,10 +492,10 @@ __device__ __forceinline__ void load_q(const AttnArgs &a, u32x4 (&qf)[8], bool r
 // transform).  False when the slot is empty or the sequence belongs to the
 // decode body (uniform over the workgroup).
 struct PrefillBlock {
-    int kvh, split, s, cu0, q_len, tq0, tq1, kv_len, ctx, kv_end, n_full, t_begin, t_end;
+    int kvh, split, s, cu0, q_len, tq0, tq1, kv_len, ctx, kv_end, n_full, first_full, t_begin, t_end;
 };
 
-template <bool CAUSAL, bool SPLIT>
+template <bool CAUSAL, bool SPLIT, bool EXT>
 __device__ __forceinline__ bool locate_block(const AttnArgs &a, int bx, int TN, PrefillBlock &B) {
     B.kvh = bx % a.num_kv_heads;
     int slot = bx / a.num_kv_heads;
@@ -489,16 +521,30 @@ __device__ __forceinline__ bool locate_block(const AttnArgs &a, int bx, int TN, 
     B.tq1 = min(B.q_len, B.tq0 + a.block_q);
     B.kv_len = a.seqused_k[lo];
     B.ctx = B.kv_len - B.q_len;                 // keys before the first query
-    // keys seen by some row / by every row of this block
+    // keys seen by some row / by every row of this block (visibility bounds
+    // grow with the row's position, so the first and last token bound them)
     B.kv_end = CAUSAL ? min(B.kv_len, B.ctx + B.tq1) : B.kv_len;
-    const int full_end = CAUSAL ? min(B.kv_len, B.ctx + B.tq0 + 1) : B.kv_len;
+    int full_end = CAUSAL ? min(B.kv_len, B.ctx + B.tq0 + 1) : B.kv_len;
+    int kv_begin = 0, full_begin = 0;
+    if (EXT) {
+        if (a.win_right >= 0) {
+            B.kv_end = min(B.kv_end, B.ctx + B.tq1 + a.win_right);
+            full_end = min(full_end, B.ctx + B.tq0 + a.win_right + 1);
+        }
+        if (a.win_left >= 0) {
+            kv_begin = max(0, B.ctx + B.tq0 - a.win_left);
+            full_begin = max(0, B.ctx + B.tq1 - 1 - a.win_left);
+        }
+    }
     const int n_tiles = max(B.kv_end, 0) / TN + ((max(B.kv_end, 0) % TN) != 0);
+    const int t_first = min(kv_begin / TN, n_tiles);
     B.n_full = max(full_end, 0) / TN;
-    B.t_begin = 0;
+    B.first_full = full_begin / TN + ((full_begin % TN) != 0);
+    B.t_begin = t_first;
     B.t_end = n_tiles;
     if (SPLIT) {
-        const int per = (n_tiles + a.num_splits - 1) / a.num_splits;
-        B.t_begin = min(n_tiles, B.split * per);
+        const int per = (n_tiles - t_first + a.num_splits - 1) / a.num_splits;
+        B.t_begin = min(n_tiles, t_first + B.split * per);
         B.t_end = min(n_tiles, B.t_begin + per);
     }
     return true;
@@ -509,7 +555,7 @@ __device__ __forceinline__ bool locate_block(const AttnArgs &a, int bx, int TN, 
 // ... of the block's range through its own two LDS stages, and the groups'
 // softmax states are merged at the end (KG = 2 gives two waves per SIMD where
 // a launch has only about one workgroup per CU).
-template <bool F16, bool FP8KV, bool CAUSAL, bool SPLIT, int KG>
+template <bool F16, bool FP8KV, bool CAUSAL, bool SPLIT, int KG, bool EXT>
 __device__ __forceinline__ void prefill_body(const AttnArgs &a, int bx, uint8_t *lds) {
     constexpr int NT = 256, TN = 64;
     constexpr int NKB = TN / 32;                // 32-key blocks per tile
@@ -543,11 +589,11 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, int bx, uint8_t 
 
     // ---------------------------------------------------------------- tiler
     PrefillBlock B;
-    if (!locate_block<CAUSAL, SPLIT>(a, bx, TN, B))
+    if (!locate_block<CAUSAL, SPLIT, EXT>(a, bx, TN, B))
         return;                                 // uniform, before any barrier
     const int kvh = B.kvh, split = B.split, s = B.s, cu0 = B.cu0;
     const int tq0 = B.tq0, tq1 = B.tq1, kv_len = B.kv_len, ctx = B.ctx, kv_end = B.kv_end;
-    const int n_full = B.n_full, t_begin = B.t_begin, t_end = B.t_end;
+    const int n_full = B.n_full, first_full = B.first_full, t_begin = B.t_begin, t_end = B.t_end;
     const int G = a.group;
     // iteration k: group g holds tile mine(k) if has(k); barriers follow the
     // iteration count, which is the same for every group
@@ -567,7 +613,17 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, int bx, uint8_t 
     const bool row_ok = t_loc < tq1;            // also false for rows past BLOCK_Q * G
     const int64_t tok = (int64_t)cu0 + t_loc;
     const int head = kvh * G + hg;
-    const int lim = !row_ok ? 0 : (CAUSAL ? min(kv_len, ctx + t_loc + 1) : kv_len);
+    int lim = !row_ok ? 0 : (CAUSAL ? min(kv_len, ctx + t_loc + 1) : kv_len);
+    RowExt ext{0, 0, 0.0f};
+    const bool alibi = EXT && a.alibi != nullptr;
+    if constexpr (EXT) {
+        const int pos = ctx + t_loc;
+        if (a.win_right >= 0)
+            lim = min(lim, pos + a.win_right + 1);
+        ext.lo = a.win_left >= 0 ? max(0, pos - a.win_left) : 0;
+        ext.pos = pos;
+        ext.sl2 = alibi ? a.alibi[head] * kLog2e : 0.0f;
+    }
     const int wv = __builtin_amdgcn_readfirstlane(wave);
     const bool wave_on = wv * 32 < (tq1 - tq0) * G;       // uniform over the wave
     u32x4 qf[8];
@@ -590,7 +646,8 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, int bx, uint8_t 
             return *(const u32x4 *)(krow + 32 * b * 256 + (((2 * ks + hl) ^ (lane & 15)) << 4));
         };
         auto vf = [&](int kk, int x) { return vfrag_lds(sV, kk, x, lane); };
-        attend_tile<F16, NKB>(st, qf, kf, vf, tile * TN, tile >= n_full, lim, c2, lane);
+        attend_tile<F16, NKB, EXT>(st, qf, kf, vf, tile * TN, tile >= n_full || (EXT && tile < first_full),
+                                   lim, c2, lane, ext, alibi);
     };
 
     if constexpr (!FP8KV) {
@@ -830,7 +887,7 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, int bx, uint8_t 
 // touch 32 key rows; whole-row loads stream about 7% faster.)  The loads of
 // unit u + NW are in flight while unit u is computed; no barrier until the
 // final merge of the waves' softmax states.
-template <bool F16, bool FP8KV, bool CAUSAL, bool SPLIT, int NW>
+template <bool F16, bool FP8KV, bool CAUSAL, bool SPLIT, int NW, bool EXT>
 __device__ __forceinline__ void decode_body(const AttnArgs &a, int bx, uint8_t *lds) {
     constexpr int NKB = 1;                      // 32-key blocks per unit
     constexpr int UK = 32 * NKB;                // keys per unit
@@ -856,14 +913,27 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, int bx, uint8_t *
         return;                                 // empty, or owned by the prefill kernel
     const int kv_len = a.seqused_k[s];
     const int ctx = kv_len - q_len;
-    const int kv_end = CAUSAL ? min(kv_len, ctx + q_len) : kv_len;
-    const int full_end = CAUSAL ? min(kv_len, ctx + 1) : kv_len;
+    int kv_end = CAUSAL ? min(kv_len, ctx + q_len) : kv_len;
+    int full_end = CAUSAL ? min(kv_len, ctx + 1) : kv_len;
+    int kv_begin = 0, full_begin = 0;
+    if (EXT) {
+        if (a.win_right >= 0) {
+            kv_end = min(kv_end, ctx + q_len + a.win_right);
+            full_end = min(full_end, ctx + a.win_right + 1);
+        }
+        if (a.win_left >= 0) {
+            kv_begin = max(0, ctx - a.win_left);
+            full_begin = max(0, ctx + q_len - 1 - a.win_left);
+        }
+    }
     const int n_units = max(kv_end, 0) / UK + ((max(kv_end, 0) % UK) != 0);
+    const int u_first = min(kv_begin / UK, n_units);
     const int n_full = max(full_end, 0) / UK;
-    int u_begin = 0, u_end = n_units;
+    const int first_full = full_begin / UK + ((full_begin % UK) != 0);
+    int u_begin = u_first, u_end = n_units;
     if (SPLIT) {
-        const int per = (n_units + a.num_splits - 1) / a.num_splits;
-        u_begin = min(n_units, split * per);
+        const int per = (n_units - u_first + a.num_splits - 1) / a.num_splits;
+        u_begin = min(n_units, u_first + split * per);
         u_end = min(n_units, u_begin + per);
     }
 
@@ -873,7 +943,17 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, int bx, uint8_t *
     const bool row_ok = tq < q_len;
     const int64_t tok = (int64_t)cu0 + tq;
     const int head = kvh * G + hg;
-    const int lim = !row_ok ? 0 : (CAUSAL ? min(kv_len, ctx + tq + 1) : kv_len);
+    int lim = !row_ok ? 0 : (CAUSAL ? min(kv_len, ctx + tq + 1) : kv_len);
+    RowExt ext{0, 0, 0.0f};
+    const bool alibi = EXT && a.alibi != nullptr;
+    if constexpr (EXT) {
+        const int pos = ctx + tq;
+        if (a.win_right >= 0)
+            lim = min(lim, pos + a.win_right + 1);
+        ext.lo = a.win_left >= 0 ? max(0, pos - a.win_left) : 0;
+        ext.pos = pos;
+        ext.sl2 = alibi && head < a.num_q_heads ? a.alibi[head] * kLog2e : 0.0f;
+    }
 
     // paging: a unit's keys lie in at most two pages (keys 0-15 and 16-31 of
     // the unit, a page holding >= 16 keys); their ids are scalar loads fetched
@@ -953,7 +1033,8 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, int bx, uint8_t *
             return *(const u32x4 *)(krow + 32 * b * 256 + (((2 * ks + hl) ^ (lane & 15)) << 4));
         };
         auto vf = [&](int kk, int x) { return vfrag_lds(sV, kk, x, lane); };
-        attend_tile<F16, NKB>(st, qf, kf, vf, u * UK, u >= n_full, lim, c2, lane);
+        attend_tile<F16, NKB, EXT>(st, qf, kf, vf, u * UK, u >= n_full || (EXT && u < first_full), lim, c2,
+                                   lane, ext, alibi);
     };
     // first unit's loads go out before Q's
     int u = u_begin + wv;
@@ -1016,15 +1097,17 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, int bx, uint8_t *
 // other.  KG = 2 (split launches with prefill work, which have few query
 // blocks per kv head): one 8-wave workgroup per CU, the prefill body's two key
 // groups (or 8 decode waves) filling the same two slots per SIMD.
-template <bool F16, bool FP8KV, bool CAUSAL, bool SPLIT, int KG>
+// EXT: the local-window / ALiBi path (a separate instantiation, so the plain
+// path carries none of its per-element work).
+template <bool F16, bool FP8KV, bool CAUSAL, bool SPLIT, int KG, bool EXT>
 __global__ __launch_bounds__(kWaves * KG * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(const AttnArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[lds_bytes(kWaves * KG)];
     const int bx = blockIdx.x;
     if (bx < a.decode_wgs)
-        decode_body<F16, FP8KV, CAUSAL, SPLIT, kWaves * KG>(a, bx, lds);
+        decode_body<F16, FP8KV, CAUSAL, SPLIT, kWaves * KG, EXT>(a, bx, lds);
     else
-        prefill_body<F16, FP8KV, CAUSAL, SPLIT, KG>(a, bx - a.decode_wgs, lds);
+        prefill_body<F16, FP8KV, CAUSAL, SPLIT, KG, EXT>(a, bx - a.decode_wgs, lds);
 }
 
 // ------------------------------------------------------------------ combine kernel
@@ -1084,27 +1167,30 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *o_part, const
 
 // ------------------------------------------------------------------ launchers
 
-template <bool F16, bool FP8KV, bool CAUSAL, bool SPLIT, int KG>
+template <bool F16, bool FP8KV, bool CAUSAL, bool SPLIT, int KG, bool EXT>
 hipError_t launch_kernel(const AttnArgs &a, dim3 grid, hipStream_t st) {
-    hipLaunchKernelGGL((attn_fwd_kernel<F16, FP8KV, CAUSAL, SPLIT, KG>), grid, dim3(kWaves * KG * 64), 0,
-                       st, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<F16, FP8KV, CAUSAL, SPLIT, KG, EXT>), grid, dim3(kWaves * KG * 64),
+                       0, st, a);
     return hipGetLastError();
 }
 
 // Two key groups only for split launches.
+template <bool F16, bool FP8KV, bool CAUSAL, bool EXT>
+hipError_t launch_shape(const AttnArgs &a, bool split, bool wide, dim3 grid, hipStream_t st) {
+    if (!split)
+        return launch_kernel<F16, FP8KV, CAUSAL, false, 1, EXT>(a, grid, st);
+    return wide ? launch_kernel<F16, FP8KV, CAUSAL, true, 2, EXT>(a, grid, st)
+                : launch_kernel<F16, FP8KV, CAUSAL, true, 1, EXT>(a, grid, st);
+}
+
 template <bool F16, bool FP8KV>
-hipError_t launch_mode(const AttnArgs &a, bool causal, bool split, bool wide, dim3 grid,
+hipError_t launch_mode(const AttnArgs &a, bool causal, bool split, bool wide, bool ext, dim3 grid,
                        hipStream_t st) {
-    if (causal) {
-        if (split)
-            return wide ? launch_kernel<F16, FP8KV, true, true, 2>(a, grid, st)
-                        : launch_kernel<F16, FP8KV, true, true, 1>(a, grid, st);
-        return launch_kernel<F16, FP8KV, true, false, 1>(a, grid, st);
-    }
-    if (split)
-        return wide ? launch_kernel<F16, FP8KV, false, true, 2>(a, grid, st)
-                    : launch_kernel<F16, FP8KV, false, true, 1>(a, grid, st);
-    return launch_kernel<F16, FP8KV, false, false, 1>(a, grid, st);
+    if (causal)
+        return ext ? launch_shape<F16, FP8KV, true, true>(a, split, wide, grid, st)
+                   : launch_shape<F16, FP8KV, true, false>(a, split, wide, grid, st);
+    return ext ? launch_shape<F16, FP8KV, false, true>(a, split, wide, grid, st)
+               : launch_shape<F16, FP8KV, false, false>(a, split, wide, grid, st);
 }
 
 }  // namespace
@@ -1113,11 +1199,12 @@ hipError_t launch_attention(const AttnArgs &a, bool q_f16, bool kv_fp8, bool cau
                             bool wide, dim3 grid, hipStream_t stream) {
     if (wide && !split)
         return hipErrorInvalidValue;
+    const bool ext = a.win_left >= 0 || a.win_right >= 0 || a.alibi != nullptr;
     if (q_f16)
-        return kv_fp8 ? launch_mode<true, true>(a, causal, split, wide, grid, stream)
-                      : launch_mode<true, false>(a, causal, split, wide, grid, stream);
-    return kv_fp8 ? launch_mode<false, true>(a, causal, split, wide, grid, stream)
-                  : launch_mode<false, false>(a, causal, split, wide, grid, stream);
+        return kv_fp8 ? launch_mode<true, true>(a, causal, split, wide, ext, grid, stream)
+                      : launch_mode<true, false>(a, causal, split, wide, ext, grid, stream);
+    return kv_fp8 ? launch_mode<false, true>(a, causal, split, wide, ext, grid, stream)
+                  : launch_mode<false, false>(a, causal, split, wide, ext, grid, stream);
 }
 
 hipError_t launch_combine(const float *o_part, const float *lse_part, int32_t num_splits,

@@ -40,6 +40,8 @@ struct AttnArgs {
     int32_t short_to_decode;       // prefill body skips sequences with q_len * G <= kDecodeRows
     int32_t decode_wgs;            // workgroups [0, decode_wgs) run the decode body, the rest prefill
     float scale_log2;              // softmax_scale * log2(e)
+    int32_t win_left, win_right;   // local attention bounds (< 0: unbounded)
+    const float *alibi;            // [Hq] ALiBi slopes, or null
 };
 
 constexpr int kPrefillBlockM = 128;   // query rows per prefill workgroup

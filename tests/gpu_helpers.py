@@ -35,6 +35,8 @@ def to_device(wl, dev="cuda"):
         "block_table": wl.block_table.to(dev),
         "k_scale": None if wl.k_scale is None else torch.tensor([wl.k_scale], dtype=torch.float32, device=dev),
         "v_scale": None if wl.v_scale is None else torch.tensor([wl.v_scale], dtype=torch.float32, device=dev),
+        "alibi": None if getattr(wl, "alibi_slopes", None) is None
+        else wl.alibi_slopes.to(torch.float32).contiguous().to(dev),
     }
     return d
 
@@ -53,6 +55,8 @@ def check_shapes(wl) -> None:
         used = (kl + bs - 1) // bs
         assert used <= bt.shape[1]
         assert np.all((bt[s, :used] >= 0) & (bt[s, :used] < NB)), "block id out of range"
+    slopes = getattr(wl, "alibi_slopes", None)
+    assert slopes is None or slopes.numel() == Hq, "one ALiBi slope per query head"
 
 
 def run(wl, dev_inputs=None, num_splits=None, want_lse=True, out=None, workspace=None, sync=True):
@@ -67,7 +71,9 @@ def run(wl, dev_inputs=None, num_splits=None, want_lse=True, out=None, workspace
                          d["block_table"], wl.max_seqlen_q, wl.max_seqlen_k, wl.softmax_scale,
                          wl.causal, d["k_scale"], d["v_scale"],
                          num_splits=wl.num_splits if num_splits is None else num_splits,
-                         lse=lse, workspace=workspace)
+                         lse=lse, workspace=workspace,
+                         window=(getattr(wl, "window_left", -1), getattr(wl, "window_right", -1)),
+                         alibi_slopes=d.get("alibi"))
     if sync:
         torch.cuda.synchronize()
     return out, lse

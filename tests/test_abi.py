@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_struct_layout(lib):
-    assert lib.ua_params_size() == ctypes.sizeof(B.AttnParams) == 216
+    assert lib.ua_params_size() == ctypes.sizeof(B.AttnParams) == 232
     assert lib.ua_plan_info_size() == ctypes.sizeof(B.PlanInfo)
     assert lib.ua_abi_version() == B.ABI_VERSION
 
@@ -170,6 +170,9 @@ def test_plan_split_prefill_is_wide(lib):
     ("kv_stride_slot", -1024, B.UA_ERR_INVALID_ARG),
     ("kv_stride_slot", 1 << 26, B.UA_ERR_UNSUPPORTED),
     ("max_seqlen_q", -1, B.UA_ERR_INVALID_ARG),
+    ("window_left", -2, B.UA_ERR_INVALID_ARG),
+    ("window_right", -5, B.UA_ERR_INVALID_ARG),
+    ("alibi_slopes", FAKE + 2, B.UA_ERR_INVALID_ARG),   # not 4-byte aligned
 ])
 def test_invalid_arguments(lib, field, value, status):
     p = base_params(**{field: value})
@@ -178,6 +181,16 @@ def test_invalid_arguments(lib, field, value, status):
     assert info.grid_x == 0
     # the launch entry point rejects the same call before touching HIP
     assert lib.ua_unified_attention(ctypes.byref(p), None) == status
+
+
+def test_window_and_alibi_accepted(lib):
+    assert plan_status(lib, base_params(window_left=0, window_right=0))[0] == B.UA_OK
+    assert plan_status(lib, base_params(window_left=4096, window_right=-1,
+                                        alibi_slopes=FAKE))[0] == B.UA_OK
+    # ALiBi distances are exact in fp32 only below 2^24 positions
+    p = base_params(alibi_slopes=FAKE, max_seqlen_k=(1 << 24) + 16,
+                    block_table_stride=((1 << 24) + 16) // 16)
+    assert plan_status(lib, p)[0] == B.UA_ERR_UNSUPPORTED
 
 
 def test_fp8_requires_scales(lib):

@@ -155,6 +155,69 @@ def test_split_prefill_two_key_groups(case):
     H.compare(wl, out, lse, what=f"key groups {case}")
 
 
+# ------------------------------------------------------------------ local attention and ALiBi
+
+MASK_CASES = [
+    # (window_left, window_right, alibi, causal, heads, kv_dtype, dtype, splits)
+    (0, 0, False, False, (4, 4), None, "bf16", 1),           # own key only
+    (0, -1, False, True, (8, 2), None, "bf16", 1),           # causal, own key only
+    (37, -1, False, True, (8, 2), None, "fp16", 1),          # causal sliding window
+    (64, -1, False, True, (16, 2), "fp8_e4m3fn", "bf16", 1),  # window = one tile
+    (100, 20, False, False, (6, 2), None, "bf16", 1),        # two-sided, G = 3
+    (-1, 5, False, False, (4, 1), None, "bf16", 1),          # right bound only
+    (-1, -1, True, True, (8, 2), None, "bf16", 1),           # ALiBi, causal
+    (-1, -1, True, False, (4, 4), None, "fp16", 1),          # ALiBi, full
+    (70, -1, True, True, (16, 2), "fp8_e4m3fn", "bf16", 1),  # ALiBi + window, fp8
+    (200, -1, False, True, (8, 2), None, "bf16", 3),         # window with splits (two key groups)
+    (33, 40, True, False, (16, 2), "fp8_e4m3fn", "bf16", 4),  # everything, split
+    (1000, -1, True, True, (8, 8), None, "bf16", 5),         # wide window, ALiBi, split, G = 1
+]
+
+
+@pytest.mark.parametrize("case", range(len(MASK_CASES)))
+def test_window_and_alibi(case):
+    left, right, alibi, causal, heads, kv_dtype, dtype, splits = MASK_CASES[case]
+    q_lens = [1, 7, 130, 3, 64, 1]
+    kv_lens = [900, 40, 400, 3, 1100, 77]
+    wl = wk.make_paged("mask", 4300 + case, q_lens, kv_lens, heads[0], heads[1],
+                       block_size=[16, 32][case % 2], dtype=dtype, kv_dtype=kv_dtype, causal=causal)
+    slopes = wk.alibi_slopes(heads[0]) if alibi else None
+    wl = wk.with_mask(wl, left, right, slopes)
+    H.say(f"mask case={case} window=({left},{right}) alibi={alibi} causal={causal} heads={heads} "
+          f"kv={kv_dtype} {dtype} splits={splits}")
+    out, lse = H.run(wl, num_splits=splits)
+    H.compare(wl, out, lse, what=f"mask {case}")
+
+
+def test_window_full_size_sampled():
+    # dense fp16 batch 4 x 4096, 32 heads, causal sliding window 1024 + ALiBi,
+    # sampled rows against the oracle row by row
+    wl = wk.with_mask(wk.config2(causal=True), 1023, -1, wk.alibi_slopes(32))
+    H.say("config2 causal window 1023 + ALiBi, sampled rows")
+    out, lse = H.run(wl)
+    H.compare(wl, out, lse, rows=H.sample_rows(wl, 96, seed=5), what="window+alibi full size")
+
+
+@pytest.mark.parametrize("splits", [1, 2])
+def test_batch_invariance_bitwise(splits):
+    # with a fixed split count, a sequence's output does not depend on the
+    # other sequences of the batch: each one run alone gives the same bits
+    wl = wk.make_paged("invariant", 4400 + splits, [1, 9, 130, 1, 40], [700, 300, 520, 65, 40], 8, 2,
+                       block_size=16, causal=True)
+    wl = wk.with_mask(wl, 150, -1, wk.alibi_slopes(8)) if splits == 2 else wl
+    H.say(f"batch invariance splits={splits}")
+    out, lse = H.run(wl, num_splits=splits)
+    cu = wl.cu_seqlens_q.tolist()
+    for s in range(wl.num_seqs):
+        one = wk.Workload(**{**wl.__dict__, "q": wl.q[cu[s]:cu[s + 1]].clone(),
+                             "cu_seqlens_q": torch.tensor([0, cu[s + 1] - cu[s]], dtype=torch.int32),
+                             "seqused_k": wl.seqused_k[s:s + 1].clone(),
+                             "block_table": wl.block_table[s:s + 1].clone()})
+        o1, l1 = H.run(one, num_splits=splits)
+        assert torch.equal(o1.view(torch.int16), out[cu[s]:cu[s + 1]].view(torch.int16)), f"seq {s} output bits"
+        assert torch.equal(l1, lse[cu[s]:cu[s + 1]]), f"seq {s} lse bits"
+
+
 def test_page_relabel_is_bitwise_invariant():
     wl = wk.make_paged("relabel", 4200, [3, 40, 1], [300, 200, 77], 8, 2, block_size=16, causal=True)
     H.say("page relabel")
