@@ -7,8 +7,10 @@ table per sequence (block_size 16).  One step = one causal call + one full
 algorithmic attention TFLOP/s: 4 * D * (visible query-key pairs) * heads,
 summed over both calls, divided by the step time.
 
-Other workloads (``--config c3|c4|c5``) are measured the same way for the
-record; c3 and c5 report KV-read GB/s.
+Other workloads (``--config c3|c4|c5|c2mask``) are measured the same way for
+the record; c3 and c5 report KV-read GB/s.  c2mask is the dense causal batch
+with a 1024-key sliding window (window_left 1023) and, as a second call, with
+ALiBi slopes; its FLOPs count only the pairs the window leaves visible.
 
 Prints ONE JSON line.  Inputs are resident in HBM before the timed region;
 K steps run back to back between two device synchronisations.  Per-launch
@@ -36,7 +38,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="c2", choices=["c2", "c3", "c4", "c5", "append"])
+    ap.add_argument("--config", default="c2", choices=["c2", "c3", "c4", "c5", "c2mask", "append"])
     ap.add_argument("--splits", type=int, default=None, help="override num_splits (c3: default the planner's choice; c5: default 32)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the oracle CPU-baseline sample")
@@ -100,6 +102,11 @@ def build_calls(cfg: str, splits_override):
                               "name": wl_c.name.replace("causal", "full")})
         return ("dense_fa2_fwd_b4_h32_n4096_d128_fp16_causal_and_full",
                 [("full", wl_f, 1), ("causal", wl_c, 1)])
+    if cfg == "c2mask":
+        wl_c = wk.config2(causal=True)
+        return ("dense_fa2_fwd_b4_h32_n4096_d128_fp16_causal_window1024_and_alibi",
+                [("window", wk.with_mask(wl_c, 1023, -1, name="c2_causal_window1024"), 1),
+                 ("alibi", wk.with_mask(wl_c, alibi=wk.alibi_slopes(32), name="c2_causal_alibi"), 1)])
     if cfg == "c3":
         wl = wk.config3()
         if splits_override is None:
@@ -152,6 +159,8 @@ def main():
             "cu": wl.cu_seqlens_q.to(dev), "kv": wl.seqused_k.to(dev), "bt": wl.block_table.to(dev),
             "ks": None if wl.k_scale is None else torch.tensor([wl.k_scale], device=dev),
             "vs": None if wl.v_scale is None else torch.tensor([wl.v_scale], device=dev),
+            "alibi": None if wl.alibi_slopes is None else wl.alibi_slopes.to(dev),
+            "window": (wl.window_left, wl.window_right),
         }
         d["out"] = torch.empty_like(d["q"])
         ws = None
@@ -164,7 +173,8 @@ def main():
     def call(wl, splits, d, ws):
         ua.unified_attention(d["q"], d["k"], d["v"], d["out"], d["cu"], d["kv"], d["bt"],
                              wl.max_seqlen_q, wl.max_seqlen_k, wl.softmax_scale, wl.causal,
-                             d["ks"], d["vs"], num_splits=splits, workspace=ws, stream=stream)
+                             d["ks"], d["vs"], num_splits=splits, workspace=ws, stream=stream,
+                             window=d["window"], alibi_slopes=d["alibi"])
 
     for _ in range(args.warmup):
         for _, wl, splits, d, ws in prepared:
@@ -196,7 +206,7 @@ def main():
                       "ms_median": float(np.median(durs)), "flops": wl.flops(),
                       "kv_bytes": wl.kv_bytes(), "splits": splits}
 
-    compute_bound = args.config in ("c2", "c4")
+    compute_bound = args.config in ("c2", "c4", "c2mask")
     if compute_bound:
         total_flops = sum(p["flops"] for p in per.values())
         value = total_flops / (ms_per_step * 1e-3) / 1e12
@@ -225,7 +235,7 @@ def main():
         "metric": metric, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp16" if args.config == "c2" else "bf16",
+        "dtype": "fp16" if args.config in ("c2", "c2mask") else "bf16",
         "data": "synthetic (seeded N(0,1) q/k/v, paged cache)",
         "config": {"workload": workload_name, "calls_per_step": [p[0] for p in prepared]},
         "roofline": roofline(dominant, f"{args.config}_{dominant}"),
@@ -393,7 +403,9 @@ def extras(args, prepared, per, result, call, stream) -> None:
         d = {"q": wl.q.to(dev), "k": wl.k_cache.to(dev), "v": wl.v_cache.to(dev),
              "cu": wl.cu_seqlens_q.to(dev), "kv": wl.seqused_k.to(dev), "bt": wl.block_table.to(dev),
              "ks": None if wl.k_scale is None else torch.tensor([wl.k_scale], device=dev),
-             "vs": None if wl.v_scale is None else torch.tensor([wl.v_scale], device=dev)}
+             "vs": None if wl.v_scale is None else torch.tensor([wl.v_scale], device=dev),
+             "alibi": None if wl.alibi_slopes is None else wl.alibi_slopes.to(dev),
+             "window": (wl.window_left, wl.window_right)}
         d["out"] = torch.empty_like(d["q"])
         import paged_varlen_flashattention_amd as ua
         ws = None
@@ -416,6 +428,13 @@ def extras(args, prepared, per, result, call, stream) -> None:
                           "GB/s": round(wl.kv_bytes() / (med * 1e-3) / 1e9, 1),
                           "hbm_frac": round(wl.kv_bytes() / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)})
         result["splits_sweep"] = sweep
+    if args.config == "c2mask":
+        # the same causal batch without window or bias, for the cost of the
+        # mask-and-bias path
+        plain = wk.with_mask(prepared[0][1], -1, -1, None, name="c2_causal_plain")
+        med, mn = run_sub(plain, 1)
+        result["plain_causal"] = {"ms_median": round(med, 4), "ms_min": round(mn, 4),
+                                  "TFLOP/s": round(plain.flops() / (med * 1e-3) / 1e12, 1)}
     if args.config == "c4":
         wl = prepared[0][1]
         ql = wl.q_lens
@@ -478,7 +497,12 @@ def row_work(wl, toks, compute_bound: bool) -> float:
     s = np.searchsorted(cu, toks, side="right") - 1
     ql = cu[s + 1] - cu[s]
     i = toks - cu[s]
-    vis = np.minimum(kv[s], kv[s] - ql + i + 1) if wl.causal else kv[s]
+    pos = kv[s] - ql + i
+    hi = np.minimum(kv[s], pos + 1) if wl.causal else kv[s]
+    if wl.window_right >= 0:
+        hi = np.minimum(hi, pos + wl.window_right + 1)
+    lo = np.maximum(pos - wl.window_left, 0) if wl.window_left >= 0 else 0
+    vis = np.maximum(hi - lo, 0)
     if compute_bound:
         return float(4.0 * wl.head_size * vis.sum())
     G = wl.num_q_heads // wl.num_kv_heads
