@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define UA_ABI_VERSION 2u
+#define UA_ABI_VERSION 3u
 
 typedef enum {
     UA_OK = 0,
@@ -65,7 +65,9 @@ typedef enum {
 } ua_dtype;
 
 /*
- * Arguments of one attention call.  Shapes use
+ * Arguments of one attention call.  Start from ua_attn_params_init(): a
+ * zero-filled struct is not the default, since window_left = window_right = 0
+ * asks for a local window of the query's own key.  Shapes use
  *   S = num_seqs, T = num_tokens, Hq = num_q_heads, Hkv = num_kv_heads,
  *   D = head_size, NB = num_blocks, bs = block_size, W = block_table_stride.
  *
@@ -101,6 +103,16 @@ typedef enum {
  *              same launch's alibi_slopes_ptr switch).  The logit of key j for
  *              query head h is softmax_scale * q . k_j - alibi_slopes[h] *
  *              |pos - j|.  Positions must stay below 2^24 (exact in fp32).
+ * fp8_compute  0 or 1; 1 needs an fp8 cache and no window / ALiBi (else
+ *              UA_ERR_UNSUPPORTED).  Sequences with q_len * (Hq / Hkv) > 32
+ *              query rows then run on the fp8 matrix cores (the fp8 attention
+ *              variants of page "flashatten takeaways EP2 工程", section
+ *              "源代码接口"): each query row (token, head) is rounded to e4m3 as
+ *              code = rne(clamp(q / s, -448, 448)) with s = max|q_row| / 448
+ *              in fp32 (s = 1 for an all-zero row), and the softmax weights
+ *              (<= 2^8) are rounded to e4m3 before P V; the row sum adds the
+ *              weights before rounding.  Shorter sequences keep the 16-bit
+ *              path.  Results differ from fp8_compute = 0 by that rounding.
  * k_scale,     device fp32 scalars, required iff kv_dtype is fp8 (else NULL):
  * v_scale      a stored code c means the value c * scale.
  * num_splits   0 = choose automatically, 1 = no split, 2..128 = split each
@@ -154,6 +166,8 @@ typedef struct ua_attn_params {
     int32_t window_left;             /* -1 = unbounded */
     int32_t window_right;            /* -1 = unbounded */
     const float *alibi_slopes;       /* [Hq] or NULL */
+    int32_t fp8_compute;             /* 0 or 1 */
+    int32_t reserved0;               /* must be 0 */
 } ua_attn_params;
 
 /* The launch the library chose for a call (filled by ua_plan).  Two kernels
@@ -281,6 +295,12 @@ const char *ua_status_string(int32_t status);
 
 /* UA_ABI_VERSION of the built library. */
 uint32_t ua_abi_version(void);
+
+/* Fill *p with the defaults: every field zero / NULL except abi_version =
+ * UA_ABI_VERSION, window_left = window_right = -1 (no local window) and
+ * num_splits = 1.  The caller then sets the tensors, shapes, strides and
+ * softmax_scale.  No-op for p == NULL. */
+void ua_attn_params_init(ua_attn_params *p);
 
 /* sizeof(ua_attn_params) and sizeof(ua_plan_info) of the built library, so a
  * binding can check its mirror of the structs. */

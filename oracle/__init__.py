@@ -34,9 +34,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(_HERE, "ua_oracle.c")
 LIB = os.path.join(_HERE, "libua_oracle.so")
 
-UAO_BF16, UAO_FP16, UAO_FP8_E4M3FN = 0, 1, 2
+UAO_BF16, UAO_FP16, UAO_FP8_E4M3FN, UAO_F64 = 0, 1, 2, 3
 _DTYPE_CODES = {torch.bfloat16: UAO_BF16, torch.float16: UAO_FP16,
-                torch.float8_e4m3fn: UAO_FP8_E4M3FN}
+                torch.float8_e4m3fn: UAO_FP8_E4M3FN, torch.float64: UAO_F64}
 _NAME_CODES = {"bf16": UAO_BF16, "fp16": UAO_FP16, "fp8_e4m3fn": UAO_FP8_E4M3FN}
 
 _lib = None
@@ -103,7 +103,8 @@ def attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
               alibi_slopes=None) -> Tuple[np.ndarray, np.ndarray]:
     """fp64 attention over a paged KV cache.
 
-    q [T, Hq, D] (bf16/fp16, any token/head strides, unit d stride);
+    q [T, Hq, D] (bf16/fp16, or float64 for queries given exactly; any
+    token/head strides, unit d stride);
     k_cache, v_cache [NB, bs, Hkv, D] (bf16/fp16/fp8_e4m3fn, unit d stride);
     cu_seqlens_q [S+1] int32; seqused_k [S] int32; block_table [S, W] int32.
     rows: optional int array [n, 2] of (token, head); default all rows,

@@ -47,7 +47,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { UAO_BF16 = 0, UAO_FP16 = 1, UAO_FP8_E4M3FN = 2 };
+enum { UAO_BF16 = 0, UAO_FP16 = 1, UAO_FP8_E4M3FN = 2, UAO_F64 = 3 };
 
 /* ---------------------------------------------------------------- decoding */
 
@@ -99,6 +99,7 @@ static double load(const void *base, int dtype, int64_t idx)
     case UAO_BF16: return dec_bf16(((const uint16_t *)base)[idx]);
     case UAO_FP16: return dec_fp16(((const uint16_t *)base)[idx]);
     case UAO_FP8_E4M3FN: return dec_e4m3fn(((const uint8_t *)base)[idx]);
+    case UAO_F64: return ((const double *)base)[idx];   /* queries given as exact doubles */
     default: return NAN;
     }
 }

@@ -15,7 +15,7 @@ import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libua.so")
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 UA_OK, UA_ERR_INVALID_ARG, UA_ERR_UNSUPPORTED, UA_ERR_WORKSPACE, UA_ERR_HIP = 0, -1, -2, -3, -4
 UA_BF16, UA_FP16, UA_FP8_E4M3FN = 0, 1, 2
@@ -24,7 +24,7 @@ _DTYPES = {torch.bfloat16: UA_BF16, torch.float16: UA_FP16, torch.float8_e4m3fn:
 # Every symbol include/ua.h declares.
 EXPORTS = ("ua_unified_attention", "ua_split_kv_combine", "ua_workspace_size", "ua_plan",
            "ua_status_string", "ua_abi_version", "ua_params_size", "ua_plan_info_size",
-           "ua_kv_append", "ua_append_params_size")
+           "ua_kv_append", "ua_append_params_size", "ua_attn_params_init")
 
 
 class UAError(RuntimeError):
@@ -55,6 +55,7 @@ class AttnParams(ctypes.Structure):
         ("num_splits", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
         ("window_left", ctypes.c_int32), ("window_right", ctypes.c_int32),
         ("alibi_slopes", ctypes.c_void_p),
+        ("fp8_compute", ctypes.c_int32), ("reserved0", ctypes.c_int32),
     ]
 
 
@@ -120,6 +121,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.ua_kv_append.argtypes = [ctypes.POINTER(AppendParams), vp]
     lib.ua_kv_append.restype = ctypes.c_int
     lib.ua_append_params_size.restype = ctypes.c_size_t
+    lib.ua_attn_params_init.argtypes = [ctypes.POINTER(AttnParams)]
+    lib.ua_attn_params_init.restype = None
     if lib.ua_abi_version() != ABI_VERSION:
         raise RuntimeError("libua.so ABI version mismatch")
     if lib.ua_params_size() != ctypes.sizeof(AttnParams) or \
@@ -154,7 +157,8 @@ def workspace_size(num_tokens: int, num_q_heads: int, head_size: int, num_splits
 
 def make_params(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table, max_seqlen_q,
                 max_seqlen_k, softmax_scale, causal, k_scale=None, v_scale=None, num_splits=1,
-                lse=None, workspace=None, window=(-1, -1), alibi_slopes=None) -> AttnParams:
+                lse=None, workspace=None, window=(-1, -1), alibi_slopes=None,
+                fp8_compute=False) -> AttnParams:
     """Fill ua_attn_params from tensors (no copies, no device work)."""
     p = AttnParams()
     p.abi_version = ABI_VERSION
@@ -191,6 +195,7 @@ def make_params(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table, 
                                      alibi_slopes.numel() != q.shape[1]):
         raise ValueError("alibi_slopes must be fp32 with one slope per query head")
     p.alibi_slopes = _ptr(alibi_slopes)
+    p.fp8_compute = int(bool(fp8_compute))
     return p
 
 
@@ -218,14 +223,15 @@ def auto_splits(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table, 
 def unified_attention(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table,
                       max_seqlen_q, max_seqlen_k, softmax_scale, causal, k_scale=None,
                       v_scale=None, num_splits=1, lse=None, workspace=None, stream=None,
-                      window=(-1, -1), alibi_slopes=None):
+                      window=(-1, -1), alibi_slopes=None, fp8_compute=False):
     """ua_unified_attention on torch device tensors; writes `out` (and `lse`).
 
     q [T, Hq, 128] bf16/fp16; k_cache, v_cache [NB, bs, Hkv, 128] (q dtype or
     float8_e4m3fn); out like q; cu_seqlens_q [S+1] int32; seqused_k [S] int32;
     block_table [S, W] int32; k_scale / v_scale 1-element fp32 device tensors for
     fp8 caches; lse optional [T, Hq] fp32; window (left, right) local attention
-    bounds (-1 = unbounded); alibi_slopes optional [Hq] fp32 device tensor.
+    bounds (-1 = unbounded); alibi_slopes optional [Hq] fp32 device tensor;
+    fp8_compute: with an fp8 cache, prefill rows on the fp8 matrix cores.
     With num_splits > 1 (or 0 = auto) a
     workspace of workspace_size(...) bytes is allocated here when none is
     given.  Enqueued on `stream` (default: torch's current stream).
@@ -241,7 +247,7 @@ def unified_attention(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_t
             workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     p = make_params(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table, max_seqlen_q,
                     max_seqlen_k, softmax_scale, causal, k_scale, v_scale, num_splits, lse, workspace,
-                    window, alibi_slopes)
+                    window, alibi_slopes, fp8_compute)
     st = load_library().ua_unified_attention(ctypes.byref(p), _stream_handle(stream))
     if st != UA_OK:
         raise UAError(st, "ua_unified_attention")

@@ -78,6 +78,11 @@ ua_status validate(const ua_attn_params *p) {
         return UA_ERR_INVALID_ARG;
     if (p->alibi_slopes && p->max_seqlen_k > (1 << 24))
         return UA_ERR_UNSUPPORTED;                             // positions exact in fp32
+    if ((p->fp8_compute != 0 && p->fp8_compute != 1) || p->reserved0 != 0)
+        return UA_ERR_INVALID_ARG;
+    if (p->fp8_compute && (p->kv_dtype != UA_FP8_E4M3FN || p->window_left >= 0 ||
+                           p->window_right >= 0 || p->alibi_slopes))
+        return UA_ERR_UNSUPPORTED;
     if (!p->q || !p->k_cache || !p->v_cache || !p->out || !p->cu_seqlens_q || !p->seqused_k ||
         !p->block_table)
         return UA_ERR_INVALID_ARG;
@@ -198,6 +203,16 @@ ua_status validate_append(const ua_append_params *p) {
 extern "C" {
 
 uint32_t ua_abi_version(void) { return UA_ABI_VERSION; }
+
+void ua_attn_params_init(ua_attn_params *p) {
+    if (p == nullptr)
+        return;
+    std::memset(p, 0, sizeof(*p));
+    p->abi_version = UA_ABI_VERSION;
+    p->window_left = -1;
+    p->window_right = -1;
+    p->num_splits = 1;
+}
 size_t ua_params_size(void) { return sizeof(ua_attn_params); }
 size_t ua_plan_info_size(void) { return sizeof(ua_plan_info); }
 size_t ua_append_params_size(void) { return sizeof(ua_append_params); }
@@ -334,6 +349,7 @@ ua_status ua_unified_attention(const ua_attn_params *p, void *stream) {
     a.win_left = p->window_left;
     a.win_right = p->window_right;
     a.alibi = p->alibi_slopes;
+    a.fp8_compute = p->fp8_compute;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool f16 = p->q_dtype == UA_FP16, fp8 = p->kv_dtype == UA_FP8_E4M3FN, causal = p->causal != 0;

@@ -89,6 +89,8 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
@@ -202,6 +204,20 @@ __device__ __forceinline__ float xhalf_sum(float v) {
 // Wait until every vector-memory load of this wave has completed (including
 // loads that write LDS directly).
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// D(32x32) += A(32x64) * B(64x32), fp8 e4m3 operands, unit block scales.
+// Lane l holds A row (B column) l % 32 and the 32 bytes k = 32 (l / 32) .. +31
+// of it; D as in mfma32.
+__device__ __forceinline__ f32x16 mfma32_f8(i32x8 a, i32x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// Four fp32 values -> four e4m3fn codes, x0 in the low byte (round to
+// nearest even).
+__device__ __forceinline__ uint32_t pack_fp8x4(float x0, float x1, float x2, float x3) {
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, lo, true);
+}
 
 // Barrier of the 4 waves of one key group of a two-group prefill workgroup, so
 // that the groups do not run in lock step (one hardware barrier per workgroup
@@ -875,6 +891,344 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, int bx, uint8_t 
     }
 }
 
+// ------------------------------------------------------------------ fp8-MFMA prefill
+
+// Opt-in fp8 compute for fp8 caches (the fp8 attention variants of page
+// "flashatten takeaways EP2 工程", section "源代码接口", and the FA3 fp8 path of
+// page "Fused Attention"): each query row is quantised to e4m3 with its own
+// scale amax / 448, K and V stay e4m3 from HBM through LDS to the matrix
+// cores, S^T = K Q^T and O^T = V^T P^T run as 32x32x64 fp8 MFMAs, and P is
+// rounded to e4m3 (weights are <= 2^8 < 448 under the lazy rescale).  The row
+// sum adds the fp32 weights before rounding, as the bf16 path does.
+//
+// LDS layouts of a 64-key tile (128-byte rows of codes, 16-byte chunks):
+//   K: chunk c of key k at c ^ gk(k), gk = ((k >> 1) & 3) | (((k >> 4) & 1) << 2);
+//   V: chunk c of key k at c ^ ((k >> 1) & 3).
+// MFMA row i of a 32-key score block reads key pk(i) = 16((i >> 2) & 1) +
+// 4(i >> 3) + (i & 3), which puts keys 16h .. 16h+15 of the block in
+// accumulator registers 0..15 of lane half h: the 32 weights a lane holds are
+// the bytes of its P^T operand, and the V^T operand gathers the same keys with
+// four 8-bit transposing reads.
+__device__ __forceinline__ int gk_swz(int k) { return ((k >> 1) & 3) | (((k >> 4) & 1) << 2); }
+__device__ __forceinline__ int gv_swz(int k) { return (k >> 1) & 3; }
+__device__ __forceinline__ int pk_row(int i) { return 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3); }
+
+template <bool F16, bool CAUSAL, bool SPLIT, int KG>
+__device__ __forceinline__ void prefill_body_f8(const AttnArgs &a, int bx, uint8_t *lds) {
+    constexpr int NT = 256, TN = 64;
+    constexpr int TB = TN * 128;                // bytes of one K (or V) tile of codes
+    constexpr int STAGE = 2 * TB;
+    static_assert(KG == 1 || KG == 2, "one or two key groups");
+
+    const int tid = threadIdx.x;
+    const int grp = KG == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid >> 8);
+    const int gtid = tid & (NT - 1);
+    const int lane = tid & 63;
+    const int wave = gtid >> 6;
+    const int hl = lane >> 5;
+    const int lc = lane & 31;
+    uint8_t *const sK0 = lds + grp * (2 * STAGE);
+    uint8_t *const sV0 = sK0 + TB;
+    uint8_t *const sK1 = sK0 + STAGE;
+    uint8_t *const sV1 = sK1 + TB;
+    // key-group barrier counters (the same place as the 16-bit body's)
+    uint32_t *const gctr = (uint32_t *)(lds + KG * 2 * (2 * TN * 256)) + grp;
+    uint32_t n_sync = 0;
+    auto loop_sync = [&]() {
+        if constexpr (KG == 1)
+            __syncthreads();
+        else
+            group_barrier(gctr, 4u * ++n_sync, lane);
+    };
+
+    PrefillBlock B;
+    if (!locate_block<CAUSAL, SPLIT, false>(a, bx, TN, B))
+        return;
+    const int kvh = B.kvh, split = B.split, s = B.s, cu0 = B.cu0;
+    const int tq0 = B.tq0, tq1 = B.tq1, kv_len = B.kv_len, ctx = B.ctx, kv_end = B.kv_end;
+    const int n_full = B.n_full, t_begin = B.t_begin, t_end = B.t_end;
+    const int G = a.group;
+    const int n_it = (t_end - t_begin + KG - 1) / KG;
+    auto mine = [&](int k) { return t_begin + grp + KG * k; };
+    auto has = [&](int k) { return mine(k) < t_end; };
+    if constexpr (KG == 2) {
+        if (tid < 2)
+            ((uint32_t *)(lds + KG * 2 * (2 * TN * 256)))[tid] = 0;
+    }
+
+    const int r = wave * 32 + lc;
+    const int tq = r / G;
+    const int hg = r - tq * G;
+    const int t_loc = tq0 + tq;
+    const bool row_ok = t_loc < tq1;
+    const int64_t tok = (int64_t)cu0 + t_loc;
+    const int head = kvh * G + hg;
+    const int lim = !row_ok ? 0 : (CAUSAL ? min(kv_len, ctx + t_loc + 1) : kv_len);
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const bool wave_on = wv * 32 < (tq1 - tq0) * G;
+
+    // Q row -> e4m3 codes: lane half hl holds d = 64 st + 32 hl + b (b < 32)
+    // of k-step st as B-operand bytes b
+    i32x8 qc[2];
+    float sq = 1.0f;
+    {
+        float qv[64];
+        if (row_ok) {
+            const uint8_t *qp = (const uint8_t *)a.q + (tok * a.q_st_tok + (int64_t)head * a.q_st_head) * 2;
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const u32x4 w = *(const u32x4 *)(qp + (64 * st + 32 * hl + 8 * c) * 2);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        float lo, hi;
+                        if constexpr (F16) {
+                            // halves taken as scalars (element access on a
+                            // bit-cast f16x2 was seen to be folded wrongly)
+                            lo = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[e] & 0xffffu));
+                            hi = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[e] >> 16));
+                        } else {
+                            lo = __uint_as_float(w[e] << 16);
+                            hi = __uint_as_float(w[e] & 0xffff0000u);
+                        }
+                        qv[32 * st + 8 * c + 2 * e] = lo;
+                        qv[32 * st + 8 * c + 2 * e + 1] = hi;
+                    }
+                }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 64; ++i)
+                qv[i] = 0.0f;
+        }
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 64; ++i)
+            amax = fmaxf(amax, __builtin_fabsf(qv[i]));
+        amax = xhalf_max(amax);
+        sq = amax > 0.0f ? amax / 448.0f : 1.0f;        // IEEE division (the code decision)
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int w = 0; w < 8; ++w) {
+                float x[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    x[e] = fminf(fmaxf(qv[32 * st + 4 * w + e] / sq, -448.0f), 448.0f);
+                qc[st][w] = (int)pack_fp8x4(x[0], x[1], x[2], x[3]);
+            }
+    }
+
+    const int32_t *btrow = a.block_table + (int64_t)s * a.bt_stride;
+    const int lbs = a.log2_block_size;
+    const int bs_mask = (1 << lbs) - 1;
+    const int last_page = (max(kv_end, 1) - 1) >> lbs;
+    const uint8_t *kbase = (const uint8_t *)a.k + (int64_t)kvh * a.kv_st_head;
+    const uint8_t *vbase = (const uint8_t *)a.v + (int64_t)kvh * a.kv_st_head;
+    const float c2 = a.scale_log2 * *a.k_scale * sq;  // code product -> log2 units
+
+    RowState st;
+    init_rows(st);
+
+    // direct loads: wave w fills keys 16w .. 16w+15 of the tile (one page)
+    // with two 8-key instructions per tensor; lane l lands at LDS byte 16 l of
+    // the instruction's 8 rows (row l / 8, chunk position l % 8) and fetches
+    // the chunk the swizzle puts there
+    const int lrow = lane >> 3, pc = lane & 7;
+    const int wrow = 16 * wv;
+    uint32_t koff[2], voff[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int kl = wrow + 8 * i + lrow;
+        koff[i] = (uint32_t)(lrow * a.kv_st_slot + 16 * (pc ^ gk_swz(kl)));
+        voff[i] = (uint32_t)(lrow * a.kv_st_slot + 16 * (pc ^ gv_swz(kl)));
+    }
+    int32_t blk = 0;
+    auto fetch_id = [&](int tile) { blk = sload(btrow + min((tile * TN + wrow) >> lbs, last_page)); };
+    auto dma_tile = [&](int tile, uint8_t *sK, uint8_t *sV) {
+        const int j = tile * TN + wrow;
+        const int64_t pofs = (int64_t)blk * a.kv_st_blk + (int64_t)(j & bs_mask) * a.kv_st_slot;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int64_t gofs = pofs + (int64_t)(8 * i) * a.kv_st_slot;
+            lds_dma16(kbase + gofs, koff[i], sK + (wrow + 8 * i) * 128);
+            lds_dma16(vbase + gofs, voff[i], sV + (wrow + 8 * i) * 128);
+        }
+    };
+    // keys at or past kv_end came from a clamped page: zero their V rows
+    auto zero_tail = [&](int tile, uint8_t *sV) {
+        if ((tile + 1) * TN > kv_end) {
+            const int row = wrow + (lane >> 2);
+            if (tile * TN + row >= kv_end) {
+                u32x4 *dst = (u32x4 *)(sV + row * 128 + 32 * (lane & 3));
+                dst[0] = u32x4{0, 0, 0, 0};
+                dst[1] = u32x4{0, 0, 0, 0};
+            }
+        }
+    };
+
+    // per-lane constants of the operand reads
+    const int krow0 = pk_row(lc);
+    const int g4 = lane >> 4;                   // 16-lane group of the transposing reads
+    const int te = (lane & 15) >> 1, tp = lane & 1;
+    auto compute = [&](int tile, const uint8_t *sK, const uint8_t *sV) {
+        f32x16 sacc[2];
+        sacc[0] = f32x16{};
+        sacc[1] = f32x16{};
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int stp = 0; stp < 2; ++stp)
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                const int kr = krow0 + 32 * b;
+                const int c0 = 4 * stp + 2 * hl;
+                const u32x4 lo = *(const u32x4 *)(sK + kr * 128 + ((c0 ^ gk_swz(kr)) << 4));
+                const u32x4 hi = *(const u32x4 *)(sK + kr * 128 + (((c0 + 1) ^ gk_swz(kr)) << 4));
+                const i32x8 av = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                  (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+                sacc[b] = mfma32_f8(av, qc[stp], sacc[b]);
+            }
+        __builtin_amdgcn_s_setprio(0);
+
+        // mask (register q of block b holds key 32 b + 16 hl + q), max, lazy
+        // rescale, weights
+        const int key0 = tile * TN;
+        if (tile >= n_full) {
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int q = 0; q < 16; ++q)
+                    if (key0 + 32 * b + 16 * hl + q >= lim)
+                        sacc[b][q] = neg_inf();
+        }
+        float mx = neg_inf();
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int q = 0; q < 16; ++q)
+                mx = fmaxf(mx, sacc[b][q]);
+        mx = xhalf_max(mx);
+        const float tmax = mx * c2;
+        const bool grow = tmax > st.m + kRescaleLog2;
+        if (__ballot(grow) != 0) {
+            const float alpha = grow ? __builtin_amdgcn_exp2f(st.m - tmax) : 1.0f;
+            st.m = grow ? tmax : st.m;
+            st.l *= alpha;
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+                st.o[x] *= alpha;
+        }
+        const float m_use = (st.m == neg_inf()) ? 0.0f : st.m;
+        float rs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const float pw = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[b][q], c2, -m_use));
+                sacc[b][q] = pw;
+                rs[q & 3] += pw;
+            }
+        st.l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+        // P^T operand: byte 16 b + q = register q of block b
+        i32x8 pf;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+            const int b = w >> 2, q0 = 4 * (w & 3);
+            pf[w] = (int)pack_fp8x4(sacc[b][q0], sacc[b][q0 + 1], sacc[b][q0 + 2], sacc[b][q0 + 3]);
+        }
+
+        // O^T += V^T P^T over the 4 d blocks; V^T bytes 8 o + e of lane half
+        // h are key 16 h + 8 (o & 1) + 32 (o >> 1) + e at d = 32 x + lane % 32
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            i32x8 av;
+#pragma unroll
+            for (int o = 0; o < 4; ++o) {
+                const int key = 16 * hl + 8 * (o & 1) + 32 * (o >> 1) + te;
+                const int c = 2 * x + (g4 & 1);
+                const uint8_t *src = sV + key * 128 + ((c ^ gv_swz(key)) << 4) + 8 * tp;
+                const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                    (__attribute__((address_space(3))) i32x2 *)(src));
+                av[2 * o] = w[0];
+                av[2 * o + 1] = w[1];
+            }
+            st.o[x] = mfma32_f8(av, pf, st.o[x]);
+        }
+    };
+
+    if (n_it > 0) {
+        if (has(0)) {
+            fetch_id(mine(0));
+            dma_tile(mine(0), sK0, sV0);
+            if (has(1))
+                fetch_id(mine(1));
+        }
+        wait_vmem();
+        if (has(0))
+            zero_tail(mine(0), sV0);
+        __syncthreads();
+    }
+    auto step = [&](int k, uint8_t *cK, uint8_t *cV, uint8_t *nK, uint8_t *nV) {
+        if (has(k + 1)) {
+            dma_tile(mine(k + 1), nK, nV);
+            if (has(k + 2))
+                fetch_id(mine(k + 2));
+        }
+        if (wave_on && has(k))
+            compute(mine(k), cK, cV);
+        if (k + 1 < n_it) {
+            wait_vmem();
+            if (has(k + 1))
+                zero_tail(mine(k + 1), nV);
+            loop_sync();
+        }
+    };
+    for (int k = 0; k < n_it; k += 2) {
+        step(k, sK0, sV0, sK1, sV1);
+        if (k + 1 < n_it)
+            step(k + 1, sK1, sV1, sK0, sV0);
+    }
+
+    // epilogue (o holds V codes x rounded weights; v_scale / l normalises)
+    if constexpr (KG == 1) {
+        if (!wave_on)
+            return;
+        const float l_row = xhalf_sum(st.l);
+        if (!row_ok)
+            return;
+        write_rows<F16, SPLIT, 4>(a, st.o, 0, st.m, l_row, *a.v_scale, tok, head, split, lane, true);
+    } else {
+        const float l_row = xhalf_sum(st.l);
+        __syncthreads();
+        float *rec = (float *)lds + wave * (kDecodeMergeRows * 64);
+        if (grp == 1) {
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    rec[(16 * x + i) * 64 + lane] = st.o[x][i];
+            rec[64 * 64 + lane] = st.m;
+            rec[65 * 64 + lane] = l_row;
+        }
+        __syncthreads();
+        if (grp == 1 || !wave_on)
+            return;
+        const float m1 = rec[64 * 64 + lane];
+        const float M = fmaxf(st.m, m1);
+        const float s0 = (st.m == neg_inf()) ? 0.0f : __builtin_amdgcn_exp2f(st.m - M);
+        const float s1 = (m1 == neg_inf()) ? 0.0f : __builtin_amdgcn_exp2f(m1 - M);
+        const float L = s0 * l_row + s1 * rec[65 * 64 + lane];
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                st.o[x][i] = s0 * st.o[x][i] + s1 * rec[(16 * x + i) * 64 + lane];
+        if (!row_ok)
+            return;
+        write_rows<F16, SPLIT, 4>(a, st.o, 0, M, L, *a.v_scale, tok, head, split, lane, true);
+    }
+}
+
 // ------------------------------------------------------------------ decode kernel
 
 // Sequences with q_len * G <= 32 rows.  Grid (S * Hkv, splits).  The NW waves
@@ -1099,13 +1453,18 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, int bx, uint8_t *
 // groups (or 8 decode waves) filling the same two slots per SIMD.
 // EXT: the local-window / ALiBi path (a separate instantiation, so the plain
 // path carries none of its per-element work).
-template <bool F16, bool FP8KV, bool CAUSAL, bool SPLIT, int KG, bool EXT>
+// F8MM (fp8 caches only, without EXT): the prefill rows use the fp8-MFMA
+// body; decode rows keep the 16-bit path.
+template <bool F16, bool FP8KV, bool CAUSAL, bool SPLIT, int KG, bool EXT, bool F8MM = false>
 __global__ __launch_bounds__(kWaves * KG * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(const AttnArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[lds_bytes(kWaves * KG)];
     const int bx = blockIdx.x;
+    static_assert(!F8MM || (FP8KV && !EXT), "fp8 compute needs an fp8 cache, no mask variants");
     if (bx < a.decode_wgs)
         decode_body<F16, FP8KV, CAUSAL, SPLIT, kWaves * KG, EXT>(a, bx, lds);
+    else if constexpr (F8MM)
+        prefill_body_f8<F16, CAUSAL, SPLIT, KG>(a, bx - a.decode_wgs, lds);
     else
         prefill_body<F16, FP8KV, CAUSAL, SPLIT, KG, EXT>(a, bx - a.decode_wgs, lds);
 }
@@ -1167,25 +1526,33 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *o_part, const
 
 // ------------------------------------------------------------------ launchers
 
-template <bool F16, bool FP8KV, bool CAUSAL, bool SPLIT, int KG, bool EXT>
+template <bool F16, bool FP8KV, bool CAUSAL, bool SPLIT, int KG, bool EXT, bool F8MM = false>
 hipError_t launch_kernel(const AttnArgs &a, dim3 grid, hipStream_t st) {
-    hipLaunchKernelGGL((attn_fwd_kernel<F16, FP8KV, CAUSAL, SPLIT, KG, EXT>), grid, dim3(kWaves * KG * 64),
-                       0, st, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<F16, FP8KV, CAUSAL, SPLIT, KG, EXT, F8MM>), grid,
+                       dim3(kWaves * KG * 64), 0, st, a);
     return hipGetLastError();
 }
 
 // Two key groups only for split launches.
-template <bool F16, bool FP8KV, bool CAUSAL, bool EXT>
+template <bool F16, bool FP8KV, bool CAUSAL, bool EXT, bool F8MM = false>
 hipError_t launch_shape(const AttnArgs &a, bool split, bool wide, dim3 grid, hipStream_t st) {
     if (!split)
-        return launch_kernel<F16, FP8KV, CAUSAL, false, 1, EXT>(a, grid, st);
-    return wide ? launch_kernel<F16, FP8KV, CAUSAL, true, 2, EXT>(a, grid, st)
-                : launch_kernel<F16, FP8KV, CAUSAL, true, 1, EXT>(a, grid, st);
+        return launch_kernel<F16, FP8KV, CAUSAL, false, 1, EXT, F8MM>(a, grid, st);
+    return wide ? launch_kernel<F16, FP8KV, CAUSAL, true, 2, EXT, F8MM>(a, grid, st)
+                : launch_kernel<F16, FP8KV, CAUSAL, true, 1, EXT, F8MM>(a, grid, st);
 }
 
 template <bool F16, bool FP8KV>
 hipError_t launch_mode(const AttnArgs &a, bool causal, bool split, bool wide, bool ext, dim3 grid,
                        hipStream_t st) {
+    if constexpr (FP8KV) {
+        if (a.fp8_compute) {
+            if (ext)
+                return hipErrorInvalidValue;
+            return causal ? launch_shape<F16, true, true, false, true>(a, split, wide, grid, st)
+                          : launch_shape<F16, true, false, false, true>(a, split, wide, grid, st);
+        }
+    }
     if (causal)
         return ext ? launch_shape<F16, FP8KV, true, true>(a, split, wide, grid, st)
                    : launch_shape<F16, FP8KV, true, false>(a, split, wide, grid, st);

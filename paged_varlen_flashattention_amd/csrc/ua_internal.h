@@ -42,6 +42,7 @@ struct AttnArgs {
     float scale_log2;              // softmax_scale * log2(e)
     int32_t win_left, win_right;   // local attention bounds (< 0: unbounded)
     const float *alibi;            // [Hq] ALiBi slopes, or null
+    int32_t fp8_compute;           // fp8 caches: prefill rows use fp8 MFMA (Q, P rounded to e4m3)
 };
 
 constexpr int kPrefillBlockM = 128;   // query rows per prefill workgroup

@@ -59,7 +59,8 @@ def check_shapes(wl) -> None:
     assert slopes is None or slopes.numel() == Hq, "one ALiBi slope per query head"
 
 
-def run(wl, dev_inputs=None, num_splits=None, want_lse=True, out=None, workspace=None, sync=True):
+def run(wl, dev_inputs=None, num_splits=None, want_lse=True, out=None, workspace=None, sync=True,
+        fp8_compute=False):
     """The HIP path on a workload; returns (out, lse) device tensors."""
     check_shapes(wl)
     d = dev_inputs or to_device(wl)
@@ -73,7 +74,7 @@ def run(wl, dev_inputs=None, num_splits=None, want_lse=True, out=None, workspace
                          num_splits=wl.num_splits if num_splits is None else num_splits,
                          lse=lse, workspace=workspace,
                          window=(getattr(wl, "window_left", -1), getattr(wl, "window_right", -1)),
-                         alibi_slopes=d.get("alibi"))
+                         alibi_slopes=d.get("alibi"), fp8_compute=fp8_compute)
     if sync:
         torch.cuda.synchronize()
     return out, lse

@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_struct_layout(lib):
-    assert lib.ua_params_size() == ctypes.sizeof(B.AttnParams) == 232
+    assert lib.ua_params_size() == ctypes.sizeof(B.AttnParams) == 240
     assert lib.ua_plan_info_size() == ctypes.sizeof(B.PlanInfo)
     assert lib.ua_abi_version() == B.ABI_VERSION
 
@@ -57,7 +57,8 @@ FAKE = 1 << 20   # 16-byte (and 256-byte) aligned fake device address
 def base_params(**kw):
     """A valid parameter set for config-3-like shapes with fake addresses."""
     p = B.AttnParams()
-    p.abi_version = B.ABI_VERSION
+    lib = B.load_library()
+    lib.ua_attn_params_init(ctypes.byref(p))
     p.q_dtype = p.kv_dtype = B.UA_BF16
     p.causal = 1
     for name in ("q", "k_cache", "v_cache", "out", "cu_seqlens_q", "seqused_k", "block_table"):
@@ -173,6 +174,9 @@ def test_plan_split_prefill_is_wide(lib):
     ("window_left", -2, B.UA_ERR_INVALID_ARG),
     ("window_right", -5, B.UA_ERR_INVALID_ARG),
     ("alibi_slopes", FAKE + 2, B.UA_ERR_INVALID_ARG),   # not 4-byte aligned
+    ("fp8_compute", 2, B.UA_ERR_INVALID_ARG),
+    ("reserved0", 1, B.UA_ERR_INVALID_ARG),
+    ("fp8_compute", 1, B.UA_ERR_UNSUPPORTED),           # bf16 cache
 ])
 def test_invalid_arguments(lib, field, value, status):
     p = base_params(**{field: value})
@@ -183,6 +187,16 @@ def test_invalid_arguments(lib, field, value, status):
     assert lib.ua_unified_attention(ctypes.byref(p), None) == status
 
 
+def test_params_init_defaults(lib):
+    p = B.AttnParams()
+    ctypes.memset(ctypes.byref(p), 0xAB, ctypes.sizeof(p))
+    lib.ua_attn_params_init(ctypes.byref(p))
+    assert p.abi_version == B.ABI_VERSION and p.num_splits == 1
+    assert (p.window_left, p.window_right) == (-1, -1)
+    assert not p.alibi_slopes and not p.q and p.fp8_compute == 0 and p.reserved0 == 0
+    lib.ua_attn_params_init(None)                           # no-op
+
+
 def test_window_and_alibi_accepted(lib):
     assert plan_status(lib, base_params(window_left=0, window_right=0))[0] == B.UA_OK
     assert plan_status(lib, base_params(window_left=4096, window_right=-1,
@@ -191,6 +205,13 @@ def test_window_and_alibi_accepted(lib):
     p = base_params(alibi_slopes=FAKE, max_seqlen_k=(1 << 24) + 16,
                     block_table_stride=((1 << 24) + 16) // 16)
     assert plan_status(lib, p)[0] == B.UA_ERR_UNSUPPORTED
+
+
+def test_fp8_compute_needs_fp8_cache_and_no_mask(lib):
+    fp8 = dict(kv_dtype=B.UA_FP8_E4M3FN, k_scale=FAKE, v_scale=FAKE, fp8_compute=1)
+    assert plan_status(lib, base_params(**fp8))[0] == B.UA_OK
+    assert plan_status(lib, base_params(window_left=10, **fp8))[0] == B.UA_ERR_UNSUPPORTED
+    assert plan_status(lib, base_params(alibi_slopes=FAKE, **fp8))[0] == B.UA_ERR_UNSUPPORTED
 
 
 def test_fp8_requires_scales(lib):
@@ -308,7 +329,7 @@ def test_append_struct_layout(lib):
 
 
 @pytest.mark.parametrize("field,value,status", [
-    ("abi_version", 3, B.UA_ERR_INVALID_ARG),
+    ("abi_version", 99, B.UA_ERR_INVALID_ARG),
     ("num_seqs", -1, B.UA_ERR_INVALID_ARG),
     ("num_tokens", -2, B.UA_ERR_INVALID_ARG),
     ("num_kv_heads", 0, B.UA_ERR_INVALID_ARG),

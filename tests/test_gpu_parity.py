@@ -218,6 +218,48 @@ def test_batch_invariance_bitwise(splits):
         assert torch.equal(l1, lse[cu[s]:cu[s + 1]]), f"seq {s} lse bits"
 
 
+# ------------------------------------------------------------------ fp8-compute mode
+
+F8_CASES = [
+    # (heads, causal, dtype, splits, block_size)
+    ((8, 2), True, "bf16", 1, 16),
+    ((16, 2), False, "bf16", 1, 32),
+    ((4, 4), True, "fp16", 1, 16),
+    ((16, 1), True, "bf16", 3, 16),         # splits: two key groups
+    ((8, 8), False, "fp16", 5, 32),
+    ((64, 8), True, "bf16", 32, 16),        # the long-context head layout, 32 splits
+]
+
+
+@pytest.mark.parametrize("case", range(len(F8_CASES)))
+def test_fp8_compute(case):
+    # prefill rows on fp8 MFMA: against the oracle with the same e4m3 query
+    # rounding; the weight rounding (relative 2^-4 per weight) is bounded per
+    # element by 2^-4 * sum_j w_j |v_j| (from the oracle's own weights) plus
+    # 0.02 for weights in the e4m3 subnormal range and the output rounding
+    import oracle.fp8_compute as f8
+    heads, causal, dtype, splits, bs = F8_CASES[case]
+    q_lens = [1, 40, 130, 3, 17, 64]
+    kv_lens = [700, 300, 900, 3, 1200, 64]
+    wl = wk.make_paged("fp8mm", 4500 + case, q_lens, kv_lens, heads[0], heads[1], block_size=bs,
+                       dtype=dtype, kv_dtype="fp8_e4m3fn", causal=causal)
+    H.say(f"fp8 compute case={case} heads={heads} causal={causal} {dtype} splits={splits} bs={bs}")
+    out, lse = H.run(wl, num_splits=splits, fp8_compute=True)
+    ref, ref_lse = f8.attention_workload_fp8(wl)
+    # |v| of an e4m3 code is the code with its sign bit cleared (exact)
+    vabs = (wl.v_cache.view(torch.uint8) & 0x7F).view(torch.float8_e4m3fn)
+    wv, _ = f8.attention_workload_fp8(wl, values=vabs)           # sum_j w_j |v_j| * v_scale
+    got = H.out_f64(out)
+    err = np.abs(got - ref)
+    bound = 2.0 ** -4 * wv + 0.02
+    worst = float((err - bound).max())
+    H.say(f"  max err {err.max():.4f}, mean err {err.mean():.5f}, worst margin {worst:.4f}")
+    assert np.all(err <= bound), f"fp8 compute beyond its bound by {worst}"
+    assert err.mean() < 5e-3
+    lerr = np.abs(lse.cpu().numpy() - ref_lse).max()
+    assert lerr < 1e-3, lerr
+
+
 def test_page_relabel_is_bitwise_invariant():
     wl = wk.make_paged("relabel", 4200, [3, 40, 1], [300, 200, 77], 8, 2, block_size=16, causal=True)
     H.say("page relabel")

@@ -81,3 +81,50 @@ def test_mask_neutral_settings(lib):
 
 def test_mask_bruteforce(lib):
     pins.check_mask_bruteforce(lib, n=40)
+
+
+# ------------------------------------------------------------------ fp8-compute mode
+
+def test_fp8_quantize_rows_matches_torch_cast():
+    """The e4m3 codes of q / s equal torch's float8_e4m3fn cast of the same
+    float32 quotients (a library routine), for bf16 and fp16 queries."""
+    import numpy as np
+    import torch
+    import oracle.fp8_compute as f8
+    import workloads as wk
+    for dtype in ("bf16", "fp16"):
+        wl = wk.make_paged("q8", 2901, [3, 40, 9], [300, 200, 50], 16, 2, block_size=16,
+                           dtype=dtype, kv_dtype="fp8_e4m3fn")
+        codes, s, deq = f8.quantize_rows(wl.q)
+        x = (wl.q.float().numpy() / s[..., None]).astype(np.float32)
+        ref = torch.from_numpy(np.clip(x, -448, 448)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(codes, ref)
+
+
+def test_fp8_quantize_rows_scale_closed_forms():
+    """The largest element of each row maps to +-448 exactly; an all-zero row
+    keeps scale 1 and zero codes; deq = code value * scale."""
+    import numpy as np
+    import torch
+    import oracle.fp8_compute as f8
+    q = torch.randn(7, 4, 128, generator=torch.Generator().manual_seed(3)).to(torch.bfloat16)
+    q[2, 1] = 0
+    codes, s, deq = f8.quantize_rows(q)
+    assert s[2, 1] == 1.0 and not codes[2, 1].any()
+    vals = deq / s[..., None]
+    amax_pos = np.abs(q.float().numpy()).argmax(axis=-1)
+    for t in range(7):
+        for h in range(4):
+            if (t, h) == (2, 1):
+                continue
+            assert abs(vals[t, h, amax_pos[t, h]]) == 448.0
+
+
+def test_fp8_compute_rows_mask():
+    """The mode applies to sequences with q_len * G > 32 rows only."""
+    import oracle.fp8_compute as f8
+    import workloads as wk
+    wl = wk.make_paged("q8m", 2902, [1, 4, 5, 0, 33], [10, 10, 10, 5, 40], 8, 1, block_size=16,
+                       kv_dtype="fp8_e4m3fn")
+    m = f8.prefill_rows_mask(wl)          # G = 8: q_len 5 -> 40 rows > 32, q_len 4 -> 32 rows
+    assert m.tolist() == [False] * 5 + [True] * 5 + [True] * 33
