@@ -11,6 +11,8 @@ Other workloads (``--config c3|c4|c5|c2mask``) are measured the same way for
 the record; c3 and c5 report KV-read GB/s.  c2mask is the dense causal batch
 with a 1024-key sliding window (window_left 1023) and, as a second call, with
 ALiBi slopes; its FLOPs count only the pairs the window leaves visible.
+c2fp8 is the dense batch with an e4m3 cache in the fp8-compute mode (queries
+and weights rounded to e4m3, fp8 MFMA), against the fp8 MFMA peak.
 
 Prints ONE JSON line.  Inputs are resident in HBM before the timed region;
 K steps run back to back between two device synchronisations.  Per-launch
@@ -30,6 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_MFMA_TFLOPS = 2516.6      # MI355X dense bf16 / fp16 MFMA
+PEAK_MFMA_FP8_TFLOPS = 5000.0  # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 
 
@@ -38,7 +41,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="c2", choices=["c2", "c3", "c4", "c5", "c2mask", "append"])
+    ap.add_argument("--config", default="c2", choices=["c2", "c3", "c4", "c5", "c2mask", "c2fp8", "append"])
     ap.add_argument("--splits", type=int, default=None, help="override num_splits (c3: default the planner's choice; c5: default 32)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the oracle CPU-baseline sample")
@@ -102,6 +105,13 @@ def build_calls(cfg: str, splits_override):
                               "name": wl_c.name.replace("causal", "full")})
         return ("dense_fa2_fwd_b4_h32_n4096_d128_fp16_causal_and_full",
                 [("full", wl_f, 1), ("causal", wl_c, 1)])
+    if cfg == "c2fp8":
+        wl_c = wk.config2(causal=True, kv_dtype="fp8_e4m3fn")
+        wl_f = wk.Workload(**{**wl_c.__dict__, "causal": False,
+                              "name": wl_c.name.replace("causal", "full")})
+        wl_c.meta["fp8_compute"] = wl_f.meta["fp8_compute"] = True
+        return ("dense_fa2_fwd_b4_h32_n4096_d128_fp16q_fp8kv_fp8compute_causal_and_full",
+                [("full", wl_f, 1), ("causal", wl_c, 1)])
     if cfg == "c2mask":
         wl_c = wk.config2(causal=True)
         return ("dense_fa2_fwd_b4_h32_n4096_d128_fp16_causal_window1024_and_alibi",
@@ -161,6 +171,7 @@ def main():
             "vs": None if wl.v_scale is None else torch.tensor([wl.v_scale], device=dev),
             "alibi": None if wl.alibi_slopes is None else wl.alibi_slopes.to(dev),
             "window": (wl.window_left, wl.window_right),
+            "f8": bool(wl.meta.get("fp8_compute", False)),
         }
         d["out"] = torch.empty_like(d["q"])
         ws = None
@@ -174,7 +185,7 @@ def main():
         ua.unified_attention(d["q"], d["k"], d["v"], d["out"], d["cu"], d["kv"], d["bt"],
                              wl.max_seqlen_q, wl.max_seqlen_k, wl.softmax_scale, wl.causal,
                              d["ks"], d["vs"], num_splits=splits, workspace=ws, stream=stream,
-                             window=d["window"], alibi_slopes=d["alibi"])
+                             window=d["window"], alibi_slopes=d["alibi"], fp8_compute=d.get("f8", False))
 
     for _ in range(args.warmup):
         for _, wl, splits, d, ws in prepared:
@@ -206,7 +217,8 @@ def main():
                       "ms_median": float(np.median(durs)), "flops": wl.flops(),
                       "kv_bytes": wl.kv_bytes(), "splits": splits}
 
-    compute_bound = args.config in ("c2", "c4", "c2mask")
+    compute_bound = args.config in ("c2", "c4", "c2mask", "c2fp8")
+    peak_mfma = PEAK_MFMA_FP8_TFLOPS if args.config == "c2fp8" else PEAK_MFMA_TFLOPS
     if compute_bound:
         total_flops = sum(p["flops"] for p in per.values())
         value = total_flops / (ms_per_step * 1e-3) / 1e12
@@ -220,8 +232,8 @@ def main():
         p = per[label]
         if compute_bound:
             ach = p["flops"] / (p["ms_mean"] * 1e-3) / 1e12
-            r = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
-                 "frac": round(ach / PEAK_MFMA_TFLOPS, 4)}
+            r = {"bound": "mfma", "achieved": round(ach, 2), "peak": peak_mfma, "unit": "TFLOP/s",
+                 "frac": round(ach / peak_mfma, 4)}
         else:
             ach = p["kv_bytes"] / (p["ms_mean"] * 1e-3) / 1e9
             r = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -235,7 +247,7 @@ def main():
         "metric": metric, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp16" if args.config in ("c2", "c2mask") else "bf16",
+        "dtype": {"c2": "fp16", "c2mask": "fp16", "c2fp8": "f8 (e4m3 operands, fp32 accumulate)"}.get(args.config, "bf16"),
         "data": "synthetic (seeded N(0,1) q/k/v, paged cache)",
         "config": {"workload": workload_name, "calls_per_step": [p[0] for p in prepared]},
         "roofline": roofline(dominant, f"{args.config}_{dominant}"),
@@ -405,7 +417,8 @@ def extras(args, prepared, per, result, call, stream) -> None:
              "ks": None if wl.k_scale is None else torch.tensor([wl.k_scale], device=dev),
              "vs": None if wl.v_scale is None else torch.tensor([wl.v_scale], device=dev),
              "alibi": None if wl.alibi_slopes is None else wl.alibi_slopes.to(dev),
-             "window": (wl.window_left, wl.window_right)}
+             "window": (wl.window_left, wl.window_right),
+             "f8": bool(wl.meta.get("fp8_compute", False))}
         d["out"] = torch.empty_like(d["q"])
         import paged_varlen_flashattention_amd as ua
         ws = None
@@ -428,6 +441,17 @@ def extras(args, prepared, per, result, call, stream) -> None:
                           "GB/s": round(wl.kv_bytes() / (med * 1e-3) / 1e9, 1),
                           "hbm_frac": round(wl.kv_bytes() / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)})
         result["splits_sweep"] = sweep
+    if args.config in ("c2fp8", "c5"):
+        # the same calls in the other compute mode (c2fp8: 16-bit compute on
+        # the e4m3 cache; c5: fp8 compute), timed apart, not part of `value`
+        other = {}
+        for label, wl, splits, d, ws in prepared:
+            w2 = wk.Workload(**{**wl.__dict__, "meta": {**wl.meta, "fp8_compute": args.config == "c5"}})
+            med, mn = run_sub(w2, splits)
+            unit = "TFLOP/s" if args.config == "c2fp8" else "GB/s"
+            val = w2.flops() / (med * 1e-3) / 1e12 if args.config == "c2fp8" else w2.kv_bytes() / (med * 1e-3) / 1e9
+            other[label] = {"ms_median": round(med, 4), "ms_min": round(mn, 4), unit: round(val, 1)}
+        result["fp8_compute" if args.config == "c5" else "sixteen_bit_compute"] = other
     if args.config == "c2mask":
         # the same causal batch without window or bias, for the cost of the
         # mask-and-bias path

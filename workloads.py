@@ -325,15 +325,18 @@ def config1() -> Workload:
                       table_mode="perm", causal=True)
 
 
-def config2(causal: bool = True, batch: int = 4, heads: int = 32, seq: int = 4096) -> Workload:
+def config2(causal: bool = True, batch: int = 4, heads: int = 32, seq: int = 4096,
+            kv_dtype: Optional[str] = None) -> Workload:
     """Dense FA2 forward (page 3 tutorial benchmark family) as a paged layout with
-    contiguous tables: batch 4, 32 heads, N 4096, D 128, fp16, causal or not."""
+    contiguous tables: batch 4, 32 heads, N 4096, D 128, fp16, causal or not.
+    kv_dtype="fp8_e4m3fn": the same draws quantised into an e4m3 cache."""
     bs = 16
     W = seq // bs
-    return make_paged(f"c2_dense_b{batch}_h{heads}_n{seq}_{'causal' if causal else 'full'}", 2,
+    tag = "" if kv_dtype is None else "_fp8kv"
+    return make_paged(f"c2_dense_b{batch}_h{heads}_n{seq}_{'causal' if causal else 'full'}{tag}", 2,
                       [seq] * batch, [seq] * batch, heads, heads, 128, block_size=bs,
-                      num_blocks=batch * W, width=W, dtype="fp16", table_mode="contiguous",
-                      causal=causal)
+                      num_blocks=batch * W, width=W, dtype="fp16", kv_dtype=kv_dtype,
+                      table_mode="contiguous", causal=causal)
 
 
 def config3_lengths(n: int = 256) -> np.ndarray:
