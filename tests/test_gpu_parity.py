@@ -260,6 +260,36 @@ def test_fp8_compute(case):
     assert lerr < 1e-3, lerr
 
 
+F8_EDGE_CASES = [
+    # (q_lens, kv_lens, heads, bs, causal, splits, zero_rows)
+    ([0, 40, 0, 33], [10, 40, 5, 100], (8, 8), 16, True, 1, False),     # empty sequences, q = kv
+    ([9, 130], [9, 131], (6, 2), 64, True, 1, False),                    # G = 3, bs 64, one-tile prefill
+    ([64, 1, 200], [64, 700, 260], (16, 2), 16, False, 7, True),         # zero query rows, more splits than tiles
+    ([128], [128], (1, 1), 32, True, 2, False),                          # G = 1, exactly two query blocks of keys
+]
+
+
+@pytest.mark.parametrize("case", range(len(F8_EDGE_CASES)))
+def test_fp8_compute_edges(case):
+    import oracle.fp8_compute as f8
+    q_lens, kv_lens, heads, bs, causal, splits, zero_rows = F8_EDGE_CASES[case]
+    wl = wk.make_paged("fp8edge", 4600 + case, q_lens, kv_lens, heads[0], heads[1], block_size=bs,
+                       kv_dtype="fp8_e4m3fn", causal=causal)
+    if zero_rows:
+        wl.q[3, :] = 0                       # whole token: every head's row is zero (scale 1)
+        wl.q[70, 1] = 0
+    H.say(f"fp8 compute edge case={case} q={q_lens} kv={kv_lens} heads={heads} bs={bs} splits={splits}")
+    out, lse = H.run(wl, num_splits=splits, fp8_compute=True)
+    ref, ref_lse = f8.attention_workload_fp8(wl)
+    vabs = (wl.v_cache.view(torch.uint8) & 0x7F).view(torch.float8_e4m3fn)
+    wv, _ = f8.attention_workload_fp8(wl, values=vabs)
+    err = np.abs(H.out_f64(out) - ref)
+    assert np.all(err <= 2.0 ** -4 * wv + 0.02), float((err - 2.0 ** -4 * wv).max())
+    fin = np.isfinite(ref_lse)
+    assert np.array_equal(fin, np.isfinite(lse.cpu().numpy()))
+    assert np.abs(lse.cpu().numpy()[fin] - ref_lse[fin]).max() < 1e-3
+
+
 def test_page_relabel_is_bitwise_invariant():
     wl = wk.make_paged("relabel", 4200, [3, 40, 1], [300, 200, 77], 8, 2, block_size=16, causal=True)
     H.say("page relabel")
