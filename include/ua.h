@@ -290,6 +290,72 @@ ua_status ua_kv_append(const ua_append_params *p, void *stream);
 /* sizeof(ua_append_params) of the built library. */
 size_t ua_append_params_size(void);
 
+/*
+ * Attention backward (page "Fused Attention", the tutorial's backward pass:
+ * the preprocess forming Delta = rowsum(O * dO), the dK/dV loop and the dQ
+ * loop, both recomputing the weights P from the forward's log-sum-exp).  For
+ * the loss sum(dO * O) of O = softmax(scale * Q K^T) V under the forward's
+ * mask, writes
+ *     dQ = scale * dS K,   dK = scale * dS^T Q,   dV = P^T dO,
+ *     dS = P * (dO V^T - Delta),
+ * where a kv head's dK and dV sum the contributions of the Hq / Hkv query
+ * heads that read it (query head h reads kv head h / (Hq / Hkv)).  Training
+ * has no cache: k and v are dense, packed like the queries.
+ *
+ * q, out, dout [T, Hq, 128] bf16 or fp16 (dtype), contiguous: sequence s owns
+ *              rows cu_seqlens_q[s] .. cu_seqlens_q[s+1] - 1.
+ * k, v         [Tk, Hkv, 128] of dtype, contiguous: sequence s owns rows
+ *              cu_seqlens_k[s] .. cu_seqlens_k[s+1] - 1 (kv_len(s) keys).
+ * lse          [T, Hq] fp32, natural-log log-sum-exp of each row as the
+ *              forward writes it (ua_attn_params.lse_out); -inf for a row
+ *              that sees no key (its gradients are 0).
+ * dq           [T, Hq, 128], dk, dv [Tk, Hkv, 128] of dtype, written in full
+ *              (keys no query sees get dK = dV = 0).
+ * causal       bottom-right alignment as in the forward: query i of a
+ *              sequence sits at key position kv_len - q_len + i.
+ * workspace    device memory of at least ua_bwd_workspace_size(T, Hq)
+ *              bytes, 256-byte aligned, no contents kept between calls.
+ *
+ * Requirements checked on the host: abi_version == UA_ABI_VERSION; dtype bf16
+ * or fp16; head_size == 128; Hq a multiple of Hkv with Hq / Hkv <= 128;
+ * non-NULL, 16-byte aligned tensors when T > 0; T * Hq and Tk * Hkv below
+ * 2^23 (UA_ERR_UNSUPPORTED beyond).  S == 0 or T + Tk == 0 is a no-op.
+ * Data-dependent violations (cu_seqlens not non-decreasing or not ending at
+ * T / Tk) are undefined behaviour.  Overlapping output and input tensors race.
+ */
+typedef struct ua_bwd_params {
+    uint32_t abi_version;
+    int32_t dtype;                   /* ua_dtype of q, k, v, out, dout, dq, dk, dv */
+    int32_t causal;
+    float softmax_scale;
+
+    const void *q;
+    const void *k;
+    const void *v;
+    const void *out;
+    const void *dout;
+    const float *lse;
+    const int32_t *cu_seqlens_q;
+    const int32_t *cu_seqlens_k;
+    void *dq;
+    void *dk;
+    void *dv;
+    void *workspace;
+    uint64_t workspace_bytes;
+
+    int32_t num_seqs, num_tokens, num_tokens_k, num_q_heads, num_kv_heads, head_size;
+} ua_bwd_params;
+
+/* Enqueue the backward kernels on `stream`.  Returns UA_OK once enqueued. */
+ua_status ua_attention_backward(const ua_bwd_params *p, void *stream);
+
+/* Workspace bytes ua_attention_backward needs: two fp32 values per (token,
+ * query head) row (LSE in log2 units and Delta), rounded up. */
+size_t ua_bwd_workspace_size(int32_t num_tokens, int32_t num_q_heads);
+
+/* sizeof(ua_bwd_params) of the built library. */
+size_t ua_bwd_params_size(void);
+
 /* Static text for a status code. */
 const char *ua_status_string(int32_t status);
 

@@ -24,7 +24,8 @@ _DTYPES = {torch.bfloat16: UA_BF16, torch.float16: UA_FP16, torch.float8_e4m3fn:
 # Every symbol include/ua.h declares.
 EXPORTS = ("ua_unified_attention", "ua_split_kv_combine", "ua_workspace_size", "ua_plan",
            "ua_status_string", "ua_abi_version", "ua_params_size", "ua_plan_info_size",
-           "ua_kv_append", "ua_append_params_size", "ua_attn_params_init")
+           "ua_kv_append", "ua_append_params_size", "ua_attn_params_init",
+           "ua_attention_backward", "ua_bwd_workspace_size", "ua_bwd_params_size")
 
 
 class UAError(RuntimeError):
@@ -56,6 +57,22 @@ class AttnParams(ctypes.Structure):
         ("window_left", ctypes.c_int32), ("window_right", ctypes.c_int32),
         ("alibi_slopes", ctypes.c_void_p),
         ("fp8_compute", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+    ]
+
+
+class BwdParams(ctypes.Structure):
+    """Mirror of ua_bwd_params (field order and types as in include/ua.h)."""
+    _fields_ = [
+        ("abi_version", ctypes.c_uint32), ("dtype", ctypes.c_int32),
+        ("causal", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("out", ctypes.c_void_p), ("dout", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+        ("cu_seqlens_q", ctypes.c_void_p), ("cu_seqlens_k", ctypes.c_void_p),
+        ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_uint64),
+        ("num_seqs", ctypes.c_int32), ("num_tokens", ctypes.c_int32),
+        ("num_tokens_k", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32), ("head_size", ctypes.c_int32),
     ]
 
 
@@ -123,11 +140,17 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.ua_append_params_size.restype = ctypes.c_size_t
     lib.ua_attn_params_init.argtypes = [ctypes.POINTER(AttnParams)]
     lib.ua_attn_params_init.restype = None
+    lib.ua_attention_backward.argtypes = [ctypes.POINTER(BwdParams), vp]
+    lib.ua_attention_backward.restype = ctypes.c_int
+    lib.ua_bwd_workspace_size.argtypes = [i32, i32]
+    lib.ua_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.ua_bwd_params_size.restype = ctypes.c_size_t
     if lib.ua_abi_version() != ABI_VERSION:
         raise RuntimeError("libua.so ABI version mismatch")
     if lib.ua_params_size() != ctypes.sizeof(AttnParams) or \
             lib.ua_plan_info_size() != ctypes.sizeof(PlanInfo) or \
-            lib.ua_append_params_size() != ctypes.sizeof(AppendParams):
+            lib.ua_append_params_size() != ctypes.sizeof(AppendParams) or \
+            lib.ua_bwd_params_size() != ctypes.sizeof(BwdParams):
         raise RuntimeError("libua.so struct layout differs from the binding")
     if path is None:
         _lib = lib
@@ -307,3 +330,49 @@ def split_kv_combine(o_partial, lse_partial, out, lse=None, stream=None):
     if st != UA_OK:
         raise UAError(st, "ua_split_kv_combine")
     return out
+
+
+def bwd_workspace_size(num_tokens: int, num_q_heads: int) -> int:
+    return int(load_library().ua_bwd_workspace_size(num_tokens, num_q_heads))
+
+
+def make_bwd_params(q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k, dq, dk, dv,
+                    softmax_scale, causal, workspace=None) -> BwdParams:
+    """ua_bwd_params for contiguous q, out, dout, dq [T, Hq, 128] and k, v, dk,
+    dv [Tk, Hkv, 128] (bf16 or fp16), lse [T, Hq] fp32, cu_seqlens_q and
+    cu_seqlens_k [S + 1] int32."""
+    p = BwdParams()
+    p.abi_version = ABI_VERSION
+    p.dtype = _DTYPES.get(q.dtype, 99)
+    p.causal = 1 if causal else 0
+    p.softmax_scale = float(softmax_scale)
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout), ("lse", lse),
+                    ("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k),
+                    ("dq", dq), ("dk", dk), ("dv", dv), ("workspace", workspace)):
+        if t is not None and name not in ("cu_seqlens_q", "cu_seqlens_k", "workspace") \
+                and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        setattr(p, name, _ptr(t))
+    p.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    p.num_seqs = cu_seqlens_q.numel() - 1
+    p.num_tokens = q.shape[0]
+    p.num_tokens_k = k.shape[0]
+    p.num_q_heads = q.shape[1]
+    p.num_kv_heads = k.shape[1]
+    p.head_size = q.shape[2]
+    return p
+
+
+def attention_backward(q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k, dq, dk, dv,
+                       softmax_scale, causal, workspace=None, stream=None):
+    """ua_attention_backward on torch device tensors (see make_bwd_params).
+    Allocates the workspace when none is given."""
+    if workspace is None:
+        n = bwd_workspace_size(q.shape[0], q.shape[1])
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    p = make_bwd_params(q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k, dq, dk, dv,
+                        softmax_scale, causal, workspace)
+    st = load_library().ua_attention_backward(ctypes.byref(p), _stream_handle(stream))
+    if st != UA_OK:
+        raise UAError(st, "ua_attention_backward")
+    return dq, dk, dv

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libua.so")
 ARCH = "gfx950"
 
-SOURCES = ["ua_attention.hip", "ua_append.hip", "ua_api.cpp"]
+SOURCES = ["ua_attention.hip", "ua_append.hip", "ua_backward.hip", "ua_api.cpp"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

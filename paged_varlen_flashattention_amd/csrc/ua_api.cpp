@@ -198,6 +198,47 @@ ua_status validate_append(const ua_append_params *p) {
     return UA_OK;
 }
 
+// backward workspace: [Hq][T] LSE2 then [Hq][T] Delta, each padded by 64 floats
+size_t bwd_half_bytes(int64_t T, int64_t Hq) { return round_up((size_t)(Hq * T + 64) * sizeof(float), kAlign); }
+
+ua_status validate_bwd(const ua_bwd_params *p) {
+    if (p == nullptr || p->abi_version != UA_ABI_VERSION)
+        return UA_ERR_INVALID_ARG;
+    if (p->dtype != UA_BF16 && p->dtype != UA_FP16)
+        return p->dtype == UA_FP8_E4M3FN ? UA_ERR_UNSUPPORTED : UA_ERR_INVALID_ARG;
+    if (p->causal != 0 && p->causal != 1)
+        return UA_ERR_INVALID_ARG;
+    if (p->num_seqs < 0 || p->num_tokens < 0 || p->num_tokens_k < 0 || p->num_q_heads <= 0 ||
+        p->num_kv_heads <= 0 || p->num_q_heads % p->num_kv_heads != 0)
+        return UA_ERR_INVALID_ARG;
+    if (p->head_size != ua::kHeadSize || p->num_q_heads / p->num_kv_heads > kMaxGroup)
+        return UA_ERR_UNSUPPORTED;
+    if (!(std::isfinite(p->softmax_scale)))
+        return UA_ERR_INVALID_ARG;
+    if (p->num_seqs == 0 || (p->num_tokens == 0 && p->num_tokens_k == 0))
+        return UA_OK;
+    if (!p->cu_seqlens_q || !p->cu_seqlens_k)
+        return UA_ERR_INVALID_ARG;
+    const void *tensors[] = {p->q, p->out, p->dout, p->dq, p->k, p->v, p->dk, p->dv};
+    const bool present[] = {p->num_tokens > 0, p->num_tokens > 0, p->num_tokens > 0, p->num_tokens > 0,
+                            p->num_tokens_k > 0, p->num_tokens_k > 0, p->num_tokens_k > 0,
+                            p->num_tokens_k > 0};
+    for (int i = 0; i < 8; ++i)
+        if (present[i] && (tensors[i] == nullptr || !aligned(tensors[i], 16)))
+            return UA_ERR_INVALID_ARG;
+    if (p->num_tokens > 0 && (p->lse == nullptr || !aligned(p->lse, 4)))
+        return UA_ERR_INVALID_ARG;
+    // 32-bit per-lane row offsets inside the kernels
+    if ((int64_t)p->num_tokens * p->num_q_heads >= (int64_t(1) << 23) ||
+        (int64_t)p->num_tokens_k * p->num_kv_heads >= (int64_t(1) << 23))
+        return UA_ERR_UNSUPPORTED;
+    if (p->num_tokens > 0 &&
+        (p->workspace == nullptr || !aligned(p->workspace, kAlign) ||
+         p->workspace_bytes < 2 * bwd_half_bytes(p->num_tokens, p->num_q_heads)))
+        return UA_ERR_WORKSPACE;
+    return UA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -245,6 +286,52 @@ ua_status ua_kv_append(const ua_append_params *p, void *stream) {
     a.log2_block_size = ilog2(p->block_size);
     if (ua::launch_append(a, p->new_dtype == UA_FP16, p->cache_dtype == UA_FP8_E4M3FN,
                           static_cast<hipStream_t>(stream)) != hipSuccess)
+        return UA_ERR_HIP;
+    return UA_OK;
+}
+
+size_t ua_bwd_params_size(void) { return sizeof(ua_bwd_params); }
+
+size_t ua_bwd_workspace_size(int32_t num_tokens, int32_t num_q_heads) {
+    if (num_tokens <= 0 || num_q_heads <= 0)
+        return 0;
+    return 2 * bwd_half_bytes(num_tokens, num_q_heads);
+}
+
+ua_status ua_attention_backward(const ua_bwd_params *p, void *stream) {
+    const ua_status st = validate_bwd(p);
+    if (st != UA_OK)
+        return st;
+    if (p->num_seqs == 0 || (p->num_tokens == 0 && p->num_tokens_k == 0))
+        return UA_OK;
+    ua::BwdArgs a{};
+    a.q = p->q;
+    a.k = p->k;
+    a.v = p->v;
+    a.o = p->out;
+    a.dout = p->dout;
+    a.lse = p->lse;
+    a.cu_seqlens_q = p->cu_seqlens_q;
+    a.cu_seqlens_k = p->cu_seqlens_k;
+    a.dq = p->dq;
+    a.dk = p->dk;
+    a.dv = p->dv;
+    a.num_seqs = p->num_seqs;
+    a.num_tokens = p->num_tokens;
+    a.num_tokens_k = p->num_tokens_k;
+    a.num_q_heads = p->num_q_heads;
+    a.num_kv_heads = p->num_kv_heads;
+    a.group = p->num_q_heads / p->num_kv_heads;
+    a.block_q = ua::kPrefillBlockM / a.group;
+    a.q_slots = p->num_tokens / a.block_q + p->num_seqs;
+    a.dkdv_wgs = (p->num_tokens_k / 128 + p->num_seqs) * p->num_kv_heads;
+    a.dq_wgs = p->num_tokens > 0 ? a.q_slots * p->num_kv_heads : 0;
+    a.scale = p->softmax_scale;
+    uint8_t *ws = static_cast<uint8_t *>(p->workspace);
+    a.lse2 = reinterpret_cast<float *>(ws);
+    a.delta = reinterpret_cast<float *>(ws + (ws ? bwd_half_bytes(p->num_tokens, p->num_q_heads) : 0));
+    if (ua::launch_backward(a, p->dtype == UA_FP16, p->causal != 0, static_cast<hipStream_t>(stream)) !=
+        hipSuccess)
         return UA_ERR_HIP;
     return UA_OK;
 }

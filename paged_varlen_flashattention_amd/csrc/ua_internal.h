@@ -86,4 +86,31 @@ struct AppendArgs {
 // (else bf16); cache_fp8: the cache holds fp8 e4m3fn codes (else new dtype).
 hipError_t launch_append(const AppendArgs &a, bool new_f16, bool cache_fp8, hipStream_t stream);
 
+// Arguments of the backward kernels (ua_backward.hip), passed by value.
+struct BwdArgs {
+    const void *q;                 // [T, Hq, 128]
+    const void *k;                 // [Tk, Hkv, 128]
+    const void *v;
+    const void *o;                 // [T, Hq, 128] forward output
+    const void *dout;              // [T, Hq, 128]
+    const float *lse;              // [T, Hq] natural log
+    const int32_t *cu_seqlens_q;   // [S + 1]
+    const int32_t *cu_seqlens_k;   // [S + 1]
+    void *dq;                      // [T, Hq, 128]
+    void *dk;                      // [Tk, Hkv, 128]
+    void *dv;
+    float *lse2;                   // workspace [Hq][T]: LSE * log2(e) (+inf: row sees no key)
+    float *delta;                  // workspace [Hq][T]: sum_d O dO
+    int32_t num_seqs, num_tokens, num_tokens_k, num_q_heads, num_kv_heads;
+    int32_t group;                 // Hq / Hkv
+    int32_t block_q;               // dQ workgroup: query tokens (128 / G)
+    int32_t q_slots;               // T / block_q + S
+    int32_t dkdv_wgs;              // (Tk / 128 + S) * Hkv
+    int32_t dq_wgs;                // q_slots * Hkv
+    float scale;
+};
+
+// Enqueue the three backward kernels (preprocess, dK/dV, dQ) on stream.
+hipError_t launch_backward(const BwdArgs &a, bool f16, bool causal, hipStream_t stream);
+
 }  // namespace ua

@@ -363,3 +363,69 @@ def test_append_empty_batch_is_noop(lib):
     assert lib.ua_kv_append(ctypes.byref(append_params(num_tokens=0, k_new=None)), None) == B.UA_OK
     assert lib.ua_kv_append(ctypes.byref(append_params(num_seqs=0, block_table=None)), None) == B.UA_OK
     assert lib.ua_kv_append(None, None) == B.UA_ERR_INVALID_ARG
+
+
+# ---------------------------------------------------------------- backward
+
+def bwd_params(**kw):
+    p = B.BwdParams()
+    p.abi_version = B.ABI_VERSION
+    p.dtype = B.UA_BF16
+    p.causal = 1
+    p.softmax_scale = 0.088
+    fake = 0x10000
+    for name in ("q", "k", "v", "out", "dout", "lse", "cu_seqlens_q", "cu_seqlens_k", "dq", "dk", "dv",
+                 "workspace"):
+        setattr(p, name, fake)
+        fake += 0x100000
+    p.num_seqs, p.num_tokens, p.num_tokens_k = 2, 100, 300
+    p.num_q_heads, p.num_kv_heads, p.head_size = 8, 2, 128
+    p.workspace_bytes = lib_bwd_ws(100, 8)
+    for k_, v_ in kw.items():
+        setattr(p, k_, v_)
+    return p
+
+
+def lib_bwd_ws(T, Hq):
+    return int(ua.load_library().ua_bwd_workspace_size(T, Hq))
+
+
+def test_bwd_struct_layout(lib):
+    assert lib.ua_bwd_params_size() == ctypes.sizeof(B.BwdParams) == 144
+
+
+def test_bwd_workspace_size(lib):
+    assert lib.ua_bwd_workspace_size(0, 8) == 0
+    n = lib.ua_bwd_workspace_size(100, 8)
+    assert n % 256 == 0 and n >= 2 * (100 * 8 + 64) * 4
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("abi_version", 99, B.UA_ERR_INVALID_ARG),
+    ("dtype", B.UA_FP8_E4M3FN, B.UA_ERR_UNSUPPORTED),
+    ("dtype", 7, B.UA_ERR_INVALID_ARG),
+    ("causal", 2, B.UA_ERR_INVALID_ARG),
+    ("head_size", 64, B.UA_ERR_UNSUPPORTED),
+    ("num_kv_heads", 3, B.UA_ERR_INVALID_ARG),
+    ("num_q_heads", 0, B.UA_ERR_INVALID_ARG),
+    ("num_tokens", -1, B.UA_ERR_INVALID_ARG),
+    ("softmax_scale", math.inf, B.UA_ERR_INVALID_ARG),
+    ("q", None, B.UA_ERR_INVALID_ARG),
+    ("dk", None, B.UA_ERR_INVALID_ARG),
+    ("lse", None, B.UA_ERR_INVALID_ARG),
+    ("cu_seqlens_k", None, B.UA_ERR_INVALID_ARG),
+    ("dq", 0x10008, B.UA_ERR_INVALID_ARG),
+    ("workspace", None, B.UA_ERR_WORKSPACE),
+    ("workspace", 0x10010, B.UA_ERR_WORKSPACE),
+    ("workspace_bytes", 1024, B.UA_ERR_WORKSPACE),
+    ("num_tokens", 1 << 21, B.UA_ERR_UNSUPPORTED),
+])
+def test_bwd_invalid_arguments(lib, field, value, status):
+    p = bwd_params(**{field: value})
+    assert lib.ua_attention_backward(ctypes.byref(p), None) == status
+
+
+def test_bwd_empty_is_noop(lib):
+    assert lib.ua_attention_backward(ctypes.byref(bwd_params(num_seqs=0)), None) == B.UA_OK
+    assert lib.ua_attention_backward(ctypes.byref(bwd_params(num_tokens=0, num_tokens_k=0)), None) == B.UA_OK
+    assert lib.ua_attention_backward(None, None) == B.UA_ERR_INVALID_ARG

@@ -462,3 +462,36 @@ def random_small(seed: int, *, max_seqs: int = 4, max_kv: int = 70, heads=(4, 2)
                       block_size=bs, num_blocks=None, dtype=dtype, kv_dtype=kv_dtype,
                       table_mode="perm", causal=c,
                       softmax_scale=float(rng.uniform(0.02, 0.2)))
+
+
+# --------------------------------------------------------------------------- backward
+
+def backward_case(seed: int, q_lens: Sequence[int], k_lens: Sequence[int], num_q_heads: int,
+                  num_kv_heads: int, dtype: str = "bf16", softmax_scale: Optional[float] = None,
+                  std: float = 1.0) -> dict:
+    """Seeded inputs of an attention backward on dense packed rows (CPU tensors):
+    q, dout [T, Hq, 128] and k, v [Tk, Hkv, 128], N(0, std^2) rounded to the
+    dtype (dout N(0, 1)); cu_seqlens_q / cu_seqlens_k [S + 1] int32 from the
+    lengths; softmax_scale (default 1 / sqrt(128)).  The page's tutorial test
+    draws N(0, 0.5^2) inputs with scale 0.5 and its benchmark N(0, 1) with
+    scale 1.3."""
+    T, Tk = int(sum(q_lens)), int(sum(k_lens))
+    sid = 7000 + int(seed)
+    q = normal_tensor(sid, 1, (T, num_q_heads, 128), dtype)
+    k = normal_tensor(sid, 2, (Tk, num_kv_heads, 128), dtype)
+    v = normal_tensor(sid, 3, (Tk, num_kv_heads, 128), dtype)
+    if std != 1.0:
+        q, k, v = ((t.float() * std).to(t.dtype) for t in (q, k, v))
+    dout = normal_tensor(sid, 4, (T, num_q_heads, 128), dtype)
+    cu_q = torch.tensor(np.concatenate([[0], np.cumsum(q_lens)]), dtype=torch.int32)
+    cu_k = torch.tensor(np.concatenate([[0], np.cumsum(k_lens)]), dtype=torch.int32)
+    return {"q": q, "k": k, "v": v, "dout": dout, "cu_seqlens_q": cu_q, "cu_seqlens_k": cu_k,
+            "q_lens": list(map(int, q_lens)), "k_lens": list(map(int, k_lens)),
+            "softmax_scale": 1.0 / math.sqrt(128) if softmax_scale is None else float(softmax_scale),
+            "dtype": dtype}
+
+
+def backward_bench(batch: int = 4, heads: int = 32, seq: int = 4096) -> dict:
+    """The page's backward benchmark (fused-attention, bwd, causal): batch 4,
+    32 heads, N 4096, fp16, N(0,1) inputs, scale 1.3; head size 128."""
+    return backward_case(8, [seq] * batch, [seq] * batch, heads, heads, "fp16", softmax_scale=1.3)
