@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="c2", choices=["c2", "c3", "c4", "c5", "c2mask", "c2fp8", "append"])
+    ap.add_argument("--config", default="c2", choices=["c2", "c3", "c4", "c5", "c2mask", "c2fp8", "append", "bwd"])
     ap.add_argument("--splits", type=int, default=None, help="override num_splits (c3: default the planner's choice; c5: default 32)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the oracle CPU-baseline sample")
@@ -69,10 +69,15 @@ def copy_calibration(nbytes: int, reps: int = 3) -> None:
     print(json.dumps({"copy_bytes": nbytes, "reps": reps}), flush=True)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(tag: str = "") -> str:
+    """Hash of the device sources behind a profiled kernel: the kernel file of
+    that workload (the append kernel, the backward kernels or the attention
+    forward) and the shared argument header."""
+    kind = tag.split("_")[0]
+    files = {"append": ["ua_append.hip"], "bwd": ["ua_backward.hip"]}.get(kind, ["ua_attention.hip"])
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_varlen_flashattention_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in sorted(files + ["ua_internal.h"]):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
@@ -91,7 +96,7 @@ def traffic_from_profiles(kernel_tag: str):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 rec[k.strip()] = v.strip()
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    if rec.get("kernel_source_hash") != kernel_source_hash(kernel_tag):
         return None
     return int(float(rec["bytes_per_launch"]))
 
@@ -145,6 +150,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(args.copy_bytes)
+        return
+    if args.config == "bwd":
+        main_bwd(args)
         return
     if args.config == "append":
         main_append(args)
@@ -348,6 +356,120 @@ def main_append(args) -> None:
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_append(wl, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def bwd_flops(q_lens, k_lens, heads: int, causal: bool, D: int = 128) -> float:
+    """Algorithmic FLOPs of a backward: 2.5x the forward's 4 * D per visible
+    (query, key) pair and head (five 2 * D products per pair: the recomputed
+    scores, dV, dP, dQ, dK)."""
+    import numpy as np
+    pairs = 0
+    for ql, kl in zip(q_lens, k_lens):
+        if causal:
+            pos = kl - ql + np.arange(ql)
+            pairs += int(np.clip(pos + 1, 0, kl).sum())
+        else:
+            pairs += ql * kl
+    return 10.0 * D * pairs * heads
+
+
+def main_bwd(args) -> None:
+    """Attention backward on the backward benchmark shape: O and LSE from one
+    (untimed) HIP forward; a step is one ua_attention_backward call (Delta
+    preprocess, dK/dV kernel, dQ kernel).  Value: algorithmic TFLOP/s."""
+    import numpy as np
+    import torch
+
+    import paged_varlen_flashattention_amd as ua
+    import workloads as wk
+    if not torch.cuda.is_available():
+        raise RuntimeError("bench.py needs a GPU")
+    ua.load_library()
+    dev = torch.device("cuda:0")
+    case = wk.backward_bench()
+    B, N, H = 4, 4096, 32
+    causal = True
+    q, k, v, do = (case[n].to(dev) for n in ("q", "k", "v", "dout"))
+    cu_q, cu_k = case["cu_seqlens_q"].to(dev), case["cu_seqlens_k"].to(dev)
+    # forward (paged view of the dense k, v: contiguous 16-key pages)
+    kc, vc = k.view(B * N // 16, 16, H, 128), v.view(B * N // 16, 16, H, 128)
+    table = (torch.arange(B * N // 16, dtype=torch.int32, device=dev).view(B, N // 16)).contiguous()
+    kl = torch.full((B,), N, dtype=torch.int32, device=dev)
+    out = torch.empty_like(q)
+    lse = torch.empty(B * N, H, dtype=torch.float32, device=dev)
+    ua.unified_attention(q, kc, vc, out, cu_q, kl, table, N, N, case["softmax_scale"], causal, lse=lse)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(ua.bwd_workspace_size(B * N, H), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    fn = lambda: ua.attention_backward(q, k, v, out, do, lse, cu_q, cu_k, dq, dk, dv,
+                                       case["softmax_scale"], causal, workspace=ws, stream=stream)
+    for _ in range(args.warmup):
+        fn()
+    torch.cuda.synchronize()
+    K = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for e0, e1 in evs:
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / K
+    durs = np.array([a.elapsed_time(b) for a, b in evs])
+    flops = bwd_flops([N] * B, [N] * B, H, causal)
+    value = flops / (ms_step * 1e-3) / 1e12
+    ach = flops / (durs.mean() * 1e-3) / 1e12
+    result = {
+        "metric": "attention backward TFLOP/s (2.5x forward FLOPs)", "value": round(value, 1),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp16",
+        "data": "synthetic (seeded N(0,1) q, k, v, dO; O and LSE from the HIP forward)",
+        "config": {"workload": "attn_bwd_dense_b4_h32_n4096_d128_causal_fp16", "batch": B, "heads": H,
+                   "seq_len": N, "softmax_scale": case["softmax_scale"]},
+        "roofline": {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(ach / PEAK_MFMA_TFLOPS, 4), "traffic": None,
+                     "launch_ms_mean": round(float(durs.mean()), 4),
+                     "kernel": "one ua_attention_backward call (preprocess + dK/dV + dQ kernels)"},
+        "per_call": {"backward": {"ms_mean": round(float(durs.mean()), 4), "ms_min": round(float(durs.min()), 4),
+                                  "ms_median": round(float(np.median(durs)), 4), "flops": flops}},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_bwd(case, causal, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline_bwd(case, causal: bool, target_s: float) -> dict:
+    """The float64 backward oracle, as it stands, on a bounded sample of the
+    same workload: whole (sequence, head) problems (4096 x 4096) cycled until
+    about target_s seconds; TFLOP/s by the same FLOP count."""
+    import numpy as np
+
+    import oracle.backward as ob
+    N = case["q_lens"][0]
+    H = case["q"].shape[1]
+    S = len(case["q_lens"])
+    work, elapsed, calls = 0.0, 0.0, 0
+    cu = np.array([0, N])
+    while elapsed < target_s:
+        s, h = calls % S, (calls // S) % H
+        sl = slice(s * N, (s + 1) * N)
+        t0 = time.perf_counter()
+        ob.attention_backward(case["q"][sl, h:h + 1], case["k"][sl, h:h + 1], case["v"][sl, h:h + 1],
+                              case["dout"][sl, h:h + 1], cu, cu, case["softmax_scale"], causal)
+        elapsed += time.perf_counter() - t0
+        work += bwd_flops([N], [N], 1, causal)
+        calls += 1
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    return {"value": round(work / elapsed / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{calls} whole (sequence, head) backward problems of {N} x {N} by the numpy float64 "
+                      f"oracle (BLAS threads {cores}), {elapsed:.1f} s on {platform.processor() or 'host'}"}
 
 
 def cpu_baseline_append(wl, target_s: float) -> dict:
