@@ -153,6 +153,14 @@ __device__ __forceinline__ void dma4(const uint8_t *base, uint32_t ofs, uint8_t 
 }
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// s_waitcnt vmcnt(0) as an instruction the compiler's wait bookkeeping
+// understands.  That bookkeeping cannot see the inline-asm DMA loads above:
+// without this after the prologue, the register operands loaded before the
+// tile loop count as in flight at the loop head, and the waits the compiler
+// then places for them inside the loop also wait, in hardware, for the next
+// tile's DMA issued just before them (the prefetch never overlaps the compute).
+__device__ __forceinline__ void vm_settled() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // largest s with cu[s] / B + s <= slot: sequence s owns the slots from
 // cu[s] / B + s on (at least ceil(len / B) of them)
 __device__ __forceinline__ int find_seq(const int32_t *cu, int num_seqs, int B, int slot) {
@@ -350,6 +358,7 @@ void bwd_dkdv_kernel(const BwdArgs a) {
         wait_vm();
         __syncthreads();
     }
+    vm_settled();
     auto step = [&](int it, uint8_t *cur, uint8_t *nxt) {
         const bool more = it + 1 < n_it;
         if (more)
@@ -526,6 +535,7 @@ void bwd_dq_kernel(const BwdArgs a) {
         wait_vm();
         __syncthreads();
     }
+    vm_settled();
     auto step = [&](int t, uint8_t *cur, uint8_t *nxt) {
         const bool more = t + 1 < n_tiles;
         if (more)
