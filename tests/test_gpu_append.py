@@ -47,7 +47,7 @@ def check(c, got_k, got_v, what):
 CASES = []
 for i, (nd, cd) in enumerate([("bf16", "bf16"), ("fp16", "fp16"), ("bf16", "fp8_e4m3fn"),
                               ("fp16", "fp8_e4m3fn")]):
-    for j, (bs, hkv) in enumerate([(16, 2), (32, 1), (64, 8)]):
+    for j, (bs, hkv) in enumerate([(16, 2), (32, 1), (64, 8), (256, 2)]):
         for sat in ((False, True) if cd == "fp8_e4m3fn" else (False,)):
             CASES.append((10 * i + j + (5 if sat else 0), nd, cd, bs, hkv, sat))
 

@@ -124,6 +124,21 @@ def test_edge_shapes(q_lens, kv_lens, heads, bs, causal):
     H.compare(wl, out, lse, what="edge")
 
 
+@pytest.mark.parametrize("bs", [128, 256, 1024])
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3fn"])
+@pytest.mark.parametrize("causal,splits", [(True, 1), (True, 3), (False, 1)])
+def test_large_pages(bs, kv_dtype, causal, splits):
+    # pages longer than a 64-key tile: several tiles (and decode units) read
+    # one page id, the last page is ragged; decode rows, a prefill block over
+    # 128 rows, a sequence inside one page and one a key past a page
+    q_lens, kv_lens = [1, 150, 7, 1], [1000, 700, 7, bs + 1]
+    wl = wk.make_paged("bigpage", 4300 + bs + (kv_dtype != "bf16"), q_lens, kv_lens, 8, 2,
+                       block_size=bs, kv_dtype=kv_dtype, causal=causal)
+    H.say(f"large pages bs={bs} kv={kv_dtype} causal={causal} splits={splits}")
+    out, lse = H.run(wl, num_splits=splits)
+    H.compare(wl, out, lse, what=f"bs {bs} {kv_dtype} splits {splits}")
+
+
 @pytest.mark.parametrize("splits", [1, 2, 3, 5, 8, 32, 0])
 def test_split_counts(splits):
     wl = wk.make_paged("splits", 4100, [1, 9, 1, 70], [900, 500, 64, 1000], 8, 2,
