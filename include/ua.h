@@ -113,8 +113,8 @@ typedef enum {
  *              (<= 2^8) are rounded to e4m3 before P V; the row sum adds the
  *              weights before rounding.  Shorter sequences keep the 16-bit
  *              path.  Results differ from fp8_compute = 0 by that rounding.
- * k_scale,     device fp32 scalars, required iff kv_dtype is fp8 (else NULL):
- * v_scale      a stored code c means the value c * scale.
+ * k_scale,     device fp32 scalars (4-byte aligned), required iff kv_dtype is
+ * v_scale      fp8 (else NULL): a stored code c means the value c * scale.
  * num_splits   0 = choose automatically, 1 = no split, 2..128 = split each
  *              query block's key range into that many contiguous chunks whose
  *              partials (fp32 output + log-sum-exp) are merged by the combine
@@ -255,8 +255,8 @@ ua_status ua_plan(const ua_attn_params *p, ua_plan_info *plan);
  * Requirements checked on the host: abi_version == UA_ABI_VERSION; non-NULL
  * k_new, v_new, k_cache, v_cache, cu_seqlens_q, seqused_k, block_table (when
  * S > 0 and T > 0); D == 128; bs a power of two in [16, 4096]; strides
- * multiples of 8 and positive; 16-byte aligned data pointers.  Rows of tokens
- * that belong to no sequence are not read.  S == 0 or T == 0 is a no-op.
+ * multiples of 8 and positive; 16-byte aligned data pointers; 4-byte aligned
+ * k_scale and v_scale.  Rows of tokens that belong to no sequence are not read.  S == 0 or T == 0 is a no-op.
  * Data-dependent violations (positions past the table, block ids outside
  * [0, NB), overlapping sequences) are undefined behaviour.
  */

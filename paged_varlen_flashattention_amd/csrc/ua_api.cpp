@@ -183,7 +183,7 @@ ua_status validate_append(const ua_append_params *p) {
         !p->block_table)
         return UA_ERR_INVALID_ARG;
     const bool fp8 = p->cache_dtype == UA_FP8_E4M3FN;
-    if (fp8 && (!p->k_scale || !p->v_scale))
+    if (fp8 && (!p->k_scale || !p->v_scale || !aligned(p->k_scale, 4) || !aligned(p->v_scale, 4)))
         return UA_ERR_INVALID_ARG;
     const int64_t strides[] = {p->new_stride_token, p->new_stride_head, p->kv_stride_block,
                                p->kv_stride_slot, p->kv_stride_head};

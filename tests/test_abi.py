@@ -357,6 +357,9 @@ def test_append_fp8_needs_scales(lib):
     assert lib.ua_kv_append(ctypes.byref(p), None) == B.UA_ERR_INVALID_ARG
     p = append_params(cache_dtype=B.UA_FP8_E4M3FN, k_scale=FAKE)
     assert lib.ua_kv_append(ctypes.byref(p), None) == B.UA_ERR_INVALID_ARG
+    # both present, one not 4-byte aligned
+    p = append_params(cache_dtype=B.UA_FP8_E4M3FN, k_scale=FAKE + 2, v_scale=FAKE)
+    assert lib.ua_kv_append(ctypes.byref(p), None) == B.UA_ERR_INVALID_ARG
 
 
 def test_append_empty_batch_is_noop(lib):
