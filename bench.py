@@ -430,7 +430,7 @@ def main_bwd(args) -> None:
         "config": {"workload": "attn_bwd_dense_b4_h32_n4096_d128_causal_fp16", "batch": B, "heads": H,
                    "seq_len": N, "softmax_scale": case["softmax_scale"]},
         "roofline": {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(ach / PEAK_MFMA_TFLOPS, 4), "traffic": None,
+                     "frac": round(ach / PEAK_MFMA_TFLOPS, 4), "traffic": traffic_from_profiles("bwd_call"),
                      "launch_ms_mean": round(float(durs.mean()), 4),
                      "kernel": "one ua_attention_backward call (preprocess + dK/dV + dQ kernels)"},
         "per_call": {"backward": {"ms_mean": round(float(durs.mean()), 4), "ms_min": round(float(durs.min()), 4),
