@@ -101,6 +101,31 @@ def traffic_from_profiles(kernel_tag: str):
     return int(float(rec["bytes_per_launch"]))
 
 
+def mfma_util_from_profiles(tag: str):
+    """Matrix-pipe utilisation of a prefill workload's kernel measured with
+    rocprofv3 (profiles/mfma_util_prefill.txt: MfmaUtil, the share of SIMD
+    cycles the MFMA unit was busy, and the clock the counters imply), or None
+    when there is no record for it or the kernel sources changed since."""
+    path = os.path.join(ROOT, "profiles", "mfma_util_prefill.txt")
+    if not os.path.exists(path):
+        return None
+    rec, header = {}, None
+    with open(path) as f:
+        for line in f:
+            if line.startswith("kernel_source_hash:"):
+                if line.split(":", 1)[1].strip() != kernel_source_hash(tag):
+                    return None
+            elif line.startswith("workload"):
+                header = line.split()
+            elif header and line.strip():
+                parts = line.split()
+                rec[parts[0]] = dict(zip(header[1:], (float(x) for x in parts[1:])))
+    r = rec.get(tag)
+    if r is None:
+        return None
+    return {"mfma_busy_pct": r["mfma_util"], "clock_ghz": r["clock_ghz"], "frac_at_clock": r["frac_clock"]}
+
+
 def build_calls(cfg: str, splits_override):
     """Returns (workload description, list of (label, workload, num_splits))."""
     import workloads as wk
@@ -248,6 +273,8 @@ def main():
                  "frac": round(ach / PEAK_HBM_GBS, 4)}
         r["traffic"] = traffic_from_profiles(tag)
         r["launch_ms_mean"] = round(p["ms_mean"], 4)
+        if compute_bound:
+            r["mfma_counters"] = mfma_util_from_profiles(tag)
         return r
 
     dominant = max(per, key=lambda k: per[k]["ms_mean"])
