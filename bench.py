@@ -168,9 +168,10 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build measures one GPU only: run bench.py with --gpus 1 "
-                          "(the attention call has no cross-GPU step; sharding is described in "
-                          "DESIGN.md)", "n_gpus": args.gpus}), flush=True)
+        print(json.dumps({"error": "bench.py measures one GPU only: run it with --gpus 1 "
+                          "(the attention call has no cross-GPU step: across GPUs it would run "
+                          "unchanged on each GPU's share of kv heads or sequences)",
+                          "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
 
     if args.copy_calibration:
