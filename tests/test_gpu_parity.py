@@ -11,6 +11,7 @@ import pytest
 import torch
 
 import gpu_helpers as H
+from paged_varlen_flashattention_amd import _binding as B
 import oracle
 import workloads as wk
 
@@ -337,6 +338,58 @@ def test_deterministic():
     a, la = H.run(wl, d, num_splits=4)
     b, lb = H.run(wl, d, num_splits=4)
     assert torch.equal(a.view(torch.int16), b.view(torch.int16)) and torch.equal(la, lb)
+
+
+@pytest.mark.parametrize("splits", [1, 4])
+def test_hip_graph_capture_replays(splits):
+    """The call holds no host synchronisation, copy or memset, so a caller can
+    capture it (and, with splits, the combine launch) into a HIP graph: after
+    the queries are overwritten in place by eager work, each replay must equal
+    an eager call bit for bit, and the last one the oracle."""
+    wl = wk.make_paged("graph", 4500 + splits, [1, 1, 37, 130], [500, 70, 300, 130], 8, 2,
+                       block_size=16, causal=True)
+    H.say(f"graph capture splits={splits}")
+    d = H.to_device(wl)
+    T, Hq = wl.num_tokens, wl.num_q_heads
+    ws = None
+    if splits > 1:
+        ws = torch.empty(B.workspace_size(T, Hq, 128, splits), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(d["q"])
+    lse = torch.empty(T, Hq, dtype=torch.float32, device="cuda")
+
+    def call():
+        B.unified_attention(d["q"], d["k_cache"], d["v_cache"], out, d["cu_seqlens_q"], d["seqused_k"],
+                            d["block_table"], wl.max_seqlen_q, wl.max_seqlen_k, wl.softmax_scale,
+                            wl.causal, d["k_scale"], d["v_scale"], num_splits=splits, lse=lse,
+                            workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+    gen = torch.Generator().manual_seed(4500 + splits)
+    for rep in range(3):
+        q_new = torch.randn(tuple(wl.q.shape), generator=gen).to(wl.q.dtype)
+        d["q"].copy_(q_new)
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        g_out, g_lse = out.clone(), lse.clone()
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        call()
+        torch.cuda.synchronize()
+        assert torch.equal(g_out.view(torch.int16), out.view(torch.int16)), f"replay {rep}: out"
+        assert torch.equal(g_lse, lse), f"replay {rep}: lse"
+    wl.q = q_new
+    H.compare(wl, out, lse, what=f"graph replay, splits {splits}")
 
 
 def test_strided_q_and_out_with_guard_canaries():
