@@ -144,3 +144,68 @@ def test_append_then_attention():
     ref, _ = oracle.attention_workload(wl)
     err = float(np.abs(out.cpu().float().numpy().astype(np.float64) - ref).max())
     assert err <= H.TOL["bf16"], err
+
+
+def test_decode_step_graph_capture():
+    """A serving decode step -- append the new tokens' k/v rows, then attend over
+    the grown cache -- captured as one HIP graph.  After fresh rows and queries
+    are written in place by eager work, each replay equals the same two calls
+    made eagerly, bit for bit (both caches, output and LSE), and the last state
+    equals the append oracle and the attention oracle."""
+    c = wk.append_case(77, num_seqs=6, max_new=3, max_prefix=300, kv_heads=2, block_size=16)
+    H.say("decode step (append + attention) graph capture")
+    dev = "cuda"
+    T, Hq = c["k_new"].shape[0], 8
+    gen = torch.Generator().manual_seed(77)
+    kn, vn = c["k_new"].to(dev), c["v_new"].to(dev)
+    kc, vc = c["k_cache"].to(dev), c["v_cache"].to(dev)
+    cu, used, bt = c["cu_seqlens_q"].to(dev), c["seqused_k"].to(dev), c["block_table"].to(dev)
+    q = torch.randn((T, Hq, 128), generator=gen).to(torch.bfloat16).to(dev)
+    out = torch.empty_like(q)
+    lse = torch.empty(T, Hq, dtype=torch.float32, device=dev)
+    q_lens = c["cu_seqlens_q"][1:] - c["cu_seqlens_q"][:-1]
+    mq, mk = int(q_lens.max()), int(c["seqused_k"].max())
+    scale = 128 ** -0.5
+
+    def step():
+        ua.kv_append(kn, vn, kc, vc, cu, used, bt, None, None)
+        ua.unified_attention(q, kc, vc, out, cu, used, bt, mq, mk, scale, True, lse=lse)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        # N(0, 1) rows, as in the attention workloads the 2e-2 bound is set for
+        k_rows = torch.randn(tuple(kn.shape), generator=gen).to(kn.dtype)
+        v_rows = torch.randn(tuple(vn.shape), generator=gen).to(vn.dtype)
+        q_rows = torch.randn(tuple(q.shape), generator=gen).to(q.dtype)
+        kn.copy_(k_rows)
+        vn.copy_(v_rows)
+        q.copy_(q_rows)
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        g = [out.clone(), lse.clone(), kc.clone(), vc.clone()]
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        step()
+        torch.cuda.synchronize()
+        for name, a, b in (("out", g[0], out), ("lse", g[1], lse), ("k_cache", g[2], kc), ("v_cache", g[3], vc)):
+            assert np.array_equal(bits(a) if a.dtype != torch.float32 else a.cpu().numpy(),
+                                  bits(b) if b.dtype != torch.float32 else b.cpu().numpy()), f"replay {rep}: {name}"
+    # every replay wrote the same slots, so the final caches are one append of
+    # the last rows onto the original contents
+    check(dict(c, k_new=k_rows, v_new=v_rows), kc.cpu(), vc.cpu(), "decode step graph")
+    ref_k, ref_v = oa.kv_append(k_rows, v_rows, c["cu_seqlens_q"], c["seqused_k"], c["block_table"],
+                                c["k_cache"], c["v_cache"], None, None)
+    wl = wk.Workload("decode_step_graph", q_rows, ref_k, ref_v, c["cu_seqlens_q"], c["seqused_k"],
+                     c["block_table"], scale, True)
+    H.compare(wl, out, lse, what="decode step graph")
