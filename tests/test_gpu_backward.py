@@ -165,3 +165,64 @@ def test_backward_full_size_sampled():
         tol = 2 * u * np.abs(dO).sum(axis=0) + 1e-3
         assert (np.abs(sum_dv - want) <= tol).all(), f"seq {s}: dV rows do not sum to the dO rows"
     assert np.isfinite(got["dq"]).all() and np.isfinite(got["dk"]).all() and np.isfinite(got["dv"]).all()
+
+
+def test_training_step_graph_capture():
+    """The forward (O, LSE) and the backward of one training step captured as
+    one HIP graph (neither call synchronises, copies to the host or clears
+    memory): after q, k, v and dO are overwritten in place by eager work, each
+    replay's O, LSE, dQ, dK and dV equal the same calls made eagerly, bit for
+    bit, and the last gradients equal the oracle's."""
+    causal = True
+    case = wk.backward_case(12, [64, 128, 16], [128, 256, 16], 8, 2, "bf16")
+    say("training step (forward + backward) graph capture")
+    kc, vc, table = _paged_view(case)
+    q, k, v, do = (_dev(case[n]) for n in ("q", "k", "v", "dout"))
+    kcd, vcd = k.view(kc.shape), v.view(vc.shape)        # the paged view of the same buffers
+    cu_q, cu_k = _dev(case["cu_seqlens_q"]), _dev(case["cu_seqlens_k"])
+    kl = _dev(torch.tensor(case["k_lens"], dtype=torch.int32))
+    tb = _dev(table)
+    T, Hq = q.shape[0], q.shape[1]
+    out = torch.empty_like(q)
+    lse = torch.empty(T, Hq, dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(ua.bwd_workspace_size(T, Hq), dtype=torch.uint8, device="cuda")
+    mq, mk, scale = max(case["q_lens"]), max(case["k_lens"]), case["softmax_scale"]
+
+    def step():
+        ua.unified_attention(q, kcd, vcd, out, cu_q, kl, tb, mq, mk, scale, causal, lse=lse)
+        ua.attention_backward(q, k, v, out, do, lse, cu_q, cu_k, dq, dk, dv, scale, causal, workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    gen = torch.Generator().manual_seed(12)
+    results = (out, lse, dq, dk, dv)
+    for rep in range(3):
+        new = {n: torch.randn(tuple(t.shape), generator=gen).to(t.dtype) for n, t in
+               (("q", q), ("k", k), ("v", v), ("dout", do))}
+        for n, t in (("q", q), ("k", k), ("v", v), ("dout", do)):
+            t.copy_(new[n])
+        for t in results:
+            t.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        snap = [t.clone() for t in results]
+        for t in results:
+            t.fill_(float("nan"))
+        step()
+        torch.cuda.synchronize()
+        for name, a, b in zip(("out", "lse", "dq", "dk", "dv"), snap, results):
+            ai = a.view(torch.int32) if a.dtype == torch.float32 else a.view(torch.int16)
+            bi = b.view(torch.int32) if b.dtype == torch.float32 else b.view(torch.int16)
+            assert torch.equal(ai, bi), f"replay {rep}: {name}"
+    got = {n: bf.to_f64(t.cpu()) for n, t in (("dq", dq), ("dk", dk), ("dv", dv))}
+    ref = oracle_case(dict(case, **new), causal)
+    check_close(got, ref, U["bf16"], "graph replay", "graph")
