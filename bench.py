@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the oracle CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="c2: skip the decode half (c3 and c5 KV-read GB/s timed after the headline)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the measurements made after the timed region (cold-cache call "
                          "times, c3 split sweep, c4 sub-batches)")
@@ -296,9 +298,77 @@ def main():
 
     if not args.no_extras:
         extras(args, prepared, per, result, call, stream)
+    cpu_items = [(label, wl, splits, None, None) for label, wl, splits, _, _ in prepared]
+    if args.config == "c2" and not args.no_decode:
+        # the decode half of the metric, after the headline's timed region
+        # (it never enters `value`): KV-read GB/s of the decode batch at the
+        # planner's split count and of the long-context batch at 32 splits
+        del prepared
+        torch.cuda.empty_cache()
+        result["decode"] = decode_half(args, call, stream)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(prepared, compute_bound, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(cpu_items, compute_bound, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def decode_half(args, call, stream) -> dict:
+    """KV-read GB/s of the two HBM-bound workloads, each with its own HBM
+    roofline object: the 256-sequence decode batch (32/8 heads, bs 16, the
+    planner's split count) and the long-context fp8 batch (2 x 131072 keys,
+    32 splits).  Per workload: `steps` warm calls back to back, bracketed by
+    HIP events on the launch stream (mean, median, min), and 10 calls with the
+    L2/MALL flushed by a 512 MB write before each (median, min)."""
+    import numpy as np
+    import torch
+
+    import paged_varlen_flashattention_amd as ua
+    dev = torch.device("cuda:0")
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    flush = lambda: scrub.fill_(1)
+    res = {}
+    for cfg, tag in (("c3", "c3_decode"), ("c5", "c5_long")):
+        name, calls = build_calls(cfg, None)
+        label, wl, splits = calls[0]
+        d = {"q": wl.q.to(dev), "k": wl.k_cache.to(dev), "v": wl.v_cache.to(dev),
+             "cu": wl.cu_seqlens_q.to(dev), "kv": wl.seqused_k.to(dev), "bt": wl.block_table.to(dev),
+             "ks": None if wl.k_scale is None else torch.tensor([wl.k_scale], device=dev),
+             "vs": None if wl.v_scale is None else torch.tensor([wl.v_scale], device=dev),
+             "alibi": None, "window": (-1, -1), "f8": False}
+        d["out"] = torch.empty_like(d["q"])
+        ws = None
+        if splits > 1:
+            ws = torch.empty(ua.workspace_size(wl.num_tokens, wl.num_q_heads, 128, splits),
+                             dtype=torch.uint8, device=dev)
+        fn = lambda: call(wl, splits, d, ws)
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for e0, e1 in evs:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        warm = np.array([a.elapsed_time(b) for a, b in evs])
+        cold = time_calls(fn, 10, stream, flush)
+        kvb = wl.kv_bytes()
+        ach = kvb / (warm.mean() * 1e-3) / 1e9
+        res[cfg] = {
+            "workload": name, "metric": "KV-read GB/s (decode)", "splits": splits,
+            "value": round(ach, 1), "unit": "GB/s", "kv_bytes": kvb,
+            "ms_mean": round(float(warm.mean()), 4), "ms_median": round(float(np.median(warm)), 4),
+            "ms_min": round(float(warm.min()), 4), "ms_cold_median": round(float(np.median(cold)), 4),
+            "ms_cold_min": round(float(cold.min()), 4),
+            "GB/s_cold_median": round(kvb / (np.median(cold) * 1e-3) / 1e9, 1),
+            "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic_from_profiles(tag),
+                         "launch_ms_mean": round(float(warm.mean()), 4),
+                         "kernel": "one ua_unified_attention call (attention kernel + split combine)"},
+        }
+        del d, ws
+        torch.cuda.empty_cache()
+    return res
 
 
 def append_bytes(k_new, k_cache) -> int:

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define UA_ABI_VERSION 3u
+#define UA_ABI_VERSION 4u
 
 typedef enum {
     UA_OK = 0,
@@ -79,9 +79,11 @@ typedef enum {
  *              kv_stride_head.  Key position j of sequence s lives in physical
  *              block block_table[s * W + j / bs], slot j % bs.
  * out          [T, Hq, D] of q_dtype; strides o_stride_token, o_stride_head.
- *              Rows of tokens that belong to no sequence are not written.
+ *              Rows of tokens that belong to no sequence (tokens at or past
+ *              cu_seqlens_q[S], padding) are not written, with or without
+ *              splits.
  * cu_seqlens_q [S + 1] int32, cu_seqlens_q[0] = 0, non-decreasing; q_len(s) =
- *              cu[s + 1] - cu[s] (0 allowed); cu[S] = T.
+ *              cu[s + 1] - cu[s] (0 allowed); cu[S] <= T.
  * seqused_k    [S] int32: kv_len(s), the number of keys of sequence s, which
  *              includes its q_len(s) new tokens (kv_len >= q_len).
  * block_table  [S, W] int32 physical block ids; entries at or past
@@ -109,10 +111,18 @@ typedef enum {
  *              variants of page "flashatten takeaways EP2 工程", section
  *              "源代码接口"): each query row (token, head) is rounded to e4m3 as
  *              code = rne(clamp(q / s, -448, 448)) with s = max|q_row| / 448
- *              in fp32 (s = 1 for an all-zero row), and the softmax weights
- *              (<= 2^8) are rounded to e4m3 before P V; the row sum adds the
- *              weights before rounding.  Shorter sequences keep the 16-bit
- *              path.  Results differ from fp8_compute = 0 by that rounding.
+ *              in fp32 (s = 1 for an all-zero row).  The softmax weights
+ *              w_j = 2^(x_j - m) (x the row's scores in log2 units) are
+ *              taken against a per-row running reference m: the maximum of
+ *              the first 64-key tile that holds a visible key, moved to a
+ *              later tile's maximum only when that exceeds m by more than 8
+ *              (so w_j <= 2^8), each key group and split keeping its own; each
+ *              w_j is rounded to the nearest e4m3fn value (ties to even,
+ *              subnormals k * 2^-9 kept) before P V, while the row sum adds
+ *              the unrounded weights.  When a row's keys fit one tile, its
+ *              output is sum_j e4m3(w_j) v_j / sum_j w_j with m the row's
+ *              maximum.  Shorter sequences keep the 16-bit path.  Results
+ *              differ from fp8_compute = 0 by these roundings.
  * k_scale,     device fp32 scalars (4-byte aligned), required iff kv_dtype is
  * v_scale      fp8 (else NULL): a stored code c means the value c * scale.
  * num_splits   0 = choose automatically, 1 = no split, 2..128 = split each
@@ -126,6 +136,14 @@ typedef enum {
  *              cannot hold.
  * lse_out      optional [T, Hq] fp32 natural-log log-sum-exp of each row's
  *              scaled scores (NULL = not written).
+ * test_barrier_timeout  0, or 1 as a test hook only.  Split launches with
+ *              prefill work run two 4-wave key groups per workgroup that
+ *              synchronise through a polled LDS counter; each wait gives up
+ *              after a bounded number of polls (2^20), and a workgroup in
+ *              which any wait gave up writes NaN to its rows (output and
+ *              log-sum-exp) instead of a result.  1 makes every such wait
+ *              give up at once, so a test can see that no timed-out wait
+ *              passes silently; every kernel still runs to its end.
  *
  * Requirements checked on the host: abi_version == UA_ABI_VERSION; non-NULL
  * q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table (when S > 0
@@ -167,7 +185,7 @@ typedef struct ua_attn_params {
     int32_t window_right;            /* -1 = unbounded */
     const float *alibi_slopes;       /* [Hq] or NULL */
     int32_t fp8_compute;             /* 0 or 1 */
-    int32_t reserved0;               /* must be 0 */
+    int32_t test_barrier_timeout;    /* 0 (1: test hook, see above) */
 } ua_attn_params;
 
 /* The launch the library chose for a call (filled by ua_plan).  Two kernels

@@ -15,7 +15,7 @@ import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libua.so")
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 UA_OK, UA_ERR_INVALID_ARG, UA_ERR_UNSUPPORTED, UA_ERR_WORKSPACE, UA_ERR_HIP = 0, -1, -2, -3, -4
 UA_BF16, UA_FP16, UA_FP8_E4M3FN = 0, 1, 2
@@ -56,7 +56,7 @@ class AttnParams(ctypes.Structure):
         ("num_splits", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
         ("window_left", ctypes.c_int32), ("window_right", ctypes.c_int32),
         ("alibi_slopes", ctypes.c_void_p),
-        ("fp8_compute", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+        ("fp8_compute", ctypes.c_int32), ("test_barrier_timeout", ctypes.c_int32),
     ]
 
 
@@ -181,7 +181,7 @@ def workspace_size(num_tokens: int, num_q_heads: int, head_size: int, num_splits
 def make_params(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table, max_seqlen_q,
                 max_seqlen_k, softmax_scale, causal, k_scale=None, v_scale=None, num_splits=1,
                 lse=None, workspace=None, window=(-1, -1), alibi_slopes=None,
-                fp8_compute=False) -> AttnParams:
+                fp8_compute=False, test_barrier_timeout=False) -> AttnParams:
     """Fill ua_attn_params from tensors (no copies, no device work)."""
     p = AttnParams()
     p.abi_version = ABI_VERSION
@@ -219,6 +219,7 @@ def make_params(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table, 
         raise ValueError("alibi_slopes must be fp32 with one slope per query head")
     p.alibi_slopes = _ptr(alibi_slopes)
     p.fp8_compute = int(bool(fp8_compute))
+    p.test_barrier_timeout = int(bool(test_barrier_timeout))
     return p
 
 
@@ -246,7 +247,8 @@ def auto_splits(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table, 
 def unified_attention(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table,
                       max_seqlen_q, max_seqlen_k, softmax_scale, causal, k_scale=None,
                       v_scale=None, num_splits=1, lse=None, workspace=None, stream=None,
-                      window=(-1, -1), alibi_slopes=None, fp8_compute=False):
+                      window=(-1, -1), alibi_slopes=None, fp8_compute=False,
+                      test_barrier_timeout=False):
     """ua_unified_attention on torch device tensors; writes `out` (and `lse`).
 
     q [T, Hq, 128] bf16/fp16; k_cache, v_cache [NB, bs, Hkv, 128] (q dtype or
@@ -270,7 +272,7 @@ def unified_attention(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_t
             workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     p = make_params(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table, max_seqlen_q,
                     max_seqlen_k, softmax_scale, causal, k_scale, v_scale, num_splits, lse, workspace,
-                    window, alibi_slopes, fp8_compute)
+                    window, alibi_slopes, fp8_compute, test_barrier_timeout)
     st = load_library().ua_unified_attention(ctypes.byref(p), _stream_handle(stream))
     if st != UA_OK:
         raise UAError(st, "ua_unified_attention")

@@ -24,6 +24,7 @@ constexpr int kMaxSplits = 128;
 constexpr int kMaxGroup = 128;
 constexpr size_t kAlign = 256;
 constexpr int kNumCUs = 256;
+constexpr int kBarrierPolls = 1 << 20;   // polls before a key-group barrier wait gives up
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 bool pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
@@ -78,7 +79,8 @@ ua_status validate(const ua_attn_params *p) {
         return UA_ERR_INVALID_ARG;
     if (p->alibi_slopes && p->max_seqlen_k > (1 << 24))
         return UA_ERR_UNSUPPORTED;                             // positions exact in fp32
-    if ((p->fp8_compute != 0 && p->fp8_compute != 1) || p->reserved0 != 0)
+    if ((p->fp8_compute != 0 && p->fp8_compute != 1) ||
+        (p->test_barrier_timeout != 0 && p->test_barrier_timeout != 1))
         return UA_ERR_INVALID_ARG;
     if (p->fp8_compute && (p->kv_dtype != UA_FP8_E4M3FN || p->window_left >= 0 ||
                            p->window_right >= 0 || p->alibi_slopes))
@@ -437,6 +439,7 @@ ua_status ua_unified_attention(const ua_attn_params *p, void *stream) {
     a.win_right = p->window_right;
     a.alibi = p->alibi_slopes;
     a.fp8_compute = p->fp8_compute;
+    a.spin_limit = p->test_barrier_timeout ? 0 : kBarrierPolls;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool f16 = p->q_dtype == UA_FP16, fp8 = p->kv_dtype == UA_FP8_E4M3FN, causal = p->causal != 0;
@@ -445,10 +448,12 @@ ua_status ua_unified_attention(const ua_attn_params *p, void *stream) {
                              s) != hipSuccess)
         return UA_ERR_HIP;
     if (split) {
+        // rows of tokens past cu_seqlens_q[S] have no partials: the combine
+        // leaves them alone, as the unsplit kernel does
         if (ua::launch_combine(a.o_part, a.lse_part, pl.splits,
                                (int64_t)p->num_tokens * p->num_q_heads, p->num_q_heads, p->out,
                                p->q_dtype == UA_FP16, p->o_stride_token, p->o_stride_head,
-                               p->lse_out, s) != hipSuccess)
+                               p->lse_out, p->cu_seqlens_q + p->num_seqs, s) != hipSuccess)
             return UA_ERR_HIP;
     }
     return UA_OK;
@@ -476,7 +481,7 @@ ua_status ua_split_kv_combine(const float *o_partial, const float *lse_partial, 
         return UA_ERR_INVALID_ARG;
     if (ua::launch_combine(o_partial, lse_partial, num_splits, (int64_t)num_tokens * num_q_heads,
                            num_q_heads, out, out_dtype == UA_FP16, o_stride_token, o_stride_head,
-                           lse_out, static_cast<hipStream_t>(stream)) != hipSuccess)
+                           lse_out, nullptr, static_cast<hipStream_t>(stream)) != hipSuccess)
         return UA_ERR_HIP;
     return UA_OK;
 }

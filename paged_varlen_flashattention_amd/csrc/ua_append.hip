@@ -97,6 +97,7 @@ template <bool F16, bool FP8>
 hipError_t launch(const AppendArgs &a, hipStream_t st) {
     const int64_t rows = (int64_t)a.num_tokens * a.num_kv_heads;
     const dim3 grid((unsigned)((rows + kRowsPerGroup - 1) / kRowsPerGroup));
+    (void)hipGetLastError();                    // report this launch's status only
     hipLaunchKernelGGL((kv_append_kernel<F16, FP8>), grid, dim3(256), 0, st, a);
     return hipGetLastError();
 }

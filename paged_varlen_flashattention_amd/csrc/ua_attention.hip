@@ -225,19 +225,34 @@ __device__ __forceinline__ uint32_t pack_fp8x4(float x0, float x1, float x2, flo
 // per group: a wave adds 1 once its own LDS writes are complete (its direct
 // loads into LDS were waited for before), then polls until the counter reaches
 // target = 4 x (barriers so far).  Every wave of a group passes the same
-// sequence of barriers; the poll count is bounded all the same, so a wave can
-// never spin forever.
-constexpr int kSpinLimit = 1 << 20;
-__device__ __forceinline__ void group_barrier(uint32_t *ctr, uint32_t target, int lane) {
+// sequence of barriers, so the wait ends; the poll count is bounded all the
+// same (spin_limit polls), so that a wave can never spin forever.  Returns
+// true when the limit was reached first: the wave then went on without the
+// barrier's guarantee, and the workgroup marks its outputs NaN (see
+// mark_lost / poison_row), so a timed-out wait never yields a silently wrong
+// result.
+__device__ __forceinline__ bool group_barrier(uint32_t *ctr, uint32_t target, int lane, int spin_limit) {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     if (lane == 0)
         __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    for (int i = 0; i < kSpinLimit; ++i) {
-        if (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target)
+    bool reached = false;
+    for (int i = 0; i < spin_limit; ++i) {
+        if (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) {
+            reached = true;
             break;
+        }
         __builtin_amdgcn_s_sleep(1);
     }
     asm volatile("" ::: "memory");
+    return !reached;
+}
+
+// A wave whose key-group barrier timed out sets the workgroup's lost flag (an
+// LDS word next to the barrier counters); the epilogue reads it after a full
+// workgroup barrier.
+__device__ __forceinline__ void mark_lost(uint32_t *flag, bool lost, int lane) {
+    if (lost && lane == 0)
+        __hip_atomic_store(flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
 // ------------------------------------------------------------------ per-tile step
@@ -479,6 +494,32 @@ __device__ __forceinline__ void write_rows(const AttnArgs &a, const f32x16 (&o)[
     }
 }
 
+// NaN into a row's output (or split partial) and log-sum-exp: the mark of a
+// workgroup whose key-group barrier timed out.  Each lane half writes its own
+// d chunks, as write_rows does.
+template <bool SPLIT>
+__device__ __forceinline__ void poison_row(const AttnArgs &a, int64_t tok, int head, int split, int lane) {
+    const int hl = lane >> 5;
+    const float nan = __builtin_nanf("");
+    if constexpr (!SPLIT) {
+        uint8_t *op = (uint8_t *)a.out + (tok * a.o_st_tok + (int64_t)head * a.o_st_head) * 2;
+        const uint32_t nan2 = 0x7fff7fffu;      // a NaN in both halves (bf16 and fp16)
+#pragma unroll
+        for (int g = 0; g < 16; ++g)
+            *(u32x2 *)(op + (8 * g + 4 * hl) * 2) = u32x2{nan2, nan2};
+        if (a.lse_out != nullptr && hl == 0)
+            a.lse_out[tok * a.num_q_heads + head] = nan;
+    } else {
+        const int64_t row = ((int64_t)split * a.num_tokens + tok) * a.num_q_heads + head;
+        float *op = a.o_part + row * HD;
+#pragma unroll
+        for (int g = 0; g < 16; ++g)
+            *(f32x4 *)(op + 8 * g + 4 * hl) = f32x4{nan, nan, nan, nan};
+        if (hl == 0)
+            a.lse_part[row] = nan;
+    }
+}
+
 // Q fragments of row (tok, head): B operand of S^T = K Q^T, k-step ks covers
 // d 16ks .. 16ks+15 (8 per lane half).  Zero for rows that do not exist.
 __device__ __forceinline__ void load_q(const AttnArgs &a, u32x4 (&qf)[8], bool row_ok, int64_t tok,
@@ -593,14 +634,17 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, int bx, uint8_t 
     uint8_t *const sV0 = sK0 + TN * 256;
     uint8_t *const sK1 = sK0 + STAGE;
     uint8_t *const sV1 = sK1 + TN * 256;
-    // key-group barrier counters, after both groups' stages
+    // key-group barrier counters (one per group), then the lost flag, after
+    // both groups' stages
     uint32_t *const gctr = (uint32_t *)(lds + KG * 2 * STAGE) + grp;
+    uint32_t *const lost_flag = (uint32_t *)(lds + KG * 2 * STAGE) + 2;
     uint32_t n_sync = 0;
+    bool lost = false;                          // a key-group barrier of this wave timed out
     auto loop_sync = [&]() {
         if constexpr (KG == 1)
             __syncthreads();
         else
-            group_barrier(gctr, 4u * ++n_sync, lane);
+            lost |= group_barrier(gctr, 4u * ++n_sync, lane, a.spin_limit);
     };
 
     // ---------------------------------------------------------------- tiler
@@ -617,7 +661,7 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, int bx, uint8_t 
     auto mine = [&](int k) { return t_begin + grp + KG * k; };
     auto has = [&](int k) { return mine(k) < t_end; };
     if constexpr (KG == 2) {
-        if (tid < 2)
+        if (tid < 3)
             ((uint32_t *)(lds + KG * 2 * STAGE))[tid] = 0;   // ordered by the first full barrier
     }
 
@@ -860,7 +904,9 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, int bx, uint8_t 
         // group 1 leaves (o, m, l) per lane in LDS; group 0 merges them into
         // its own state (both hold the same rows in the same lanes)
         const float l_row = xhalf_sum(st.l);
+        mark_lost(lost_flag, lost, lane);
         __syncthreads();                        // both groups are done with their stages
+        const bool wg_lost = __hip_atomic_load(lost_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0;
         float *rec = (float *)lds + wave * (kDecodeMergeRows * 64);
         if (grp == 1) {
 #pragma unroll
@@ -886,6 +932,10 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, int bx, uint8_t 
                 st.o[x][i] = s0 * st.o[x][i] + s1 * rec[(16 * x + i) * 64 + lane];
         if (!row_ok)
             return;
+        if (wg_lost) {
+            poison_row<SPLIT>(a, tok, head, split, lane);
+            return;
+        }
         write_rows<F16, SPLIT, 4>(a, st.o, 0, M, L, FP8KV ? *a.v_scale : 1.0f, tok, head, split,
                                   lane, true);
     }
@@ -931,14 +981,17 @@ __device__ __forceinline__ void prefill_body_f8(const AttnArgs &a, int bx, uint8
     uint8_t *const sV0 = sK0 + TB;
     uint8_t *const sK1 = sK0 + STAGE;
     uint8_t *const sV1 = sK1 + TB;
-    // key-group barrier counters (the same place as the 16-bit body's)
+    // key-group barrier counters and the lost flag (the same place as the
+    // 16-bit body's)
     uint32_t *const gctr = (uint32_t *)(lds + KG * 2 * (2 * TN * 256)) + grp;
+    uint32_t *const lost_flag = (uint32_t *)(lds + KG * 2 * (2 * TN * 256)) + 2;
     uint32_t n_sync = 0;
+    bool lost = false;
     auto loop_sync = [&]() {
         if constexpr (KG == 1)
             __syncthreads();
         else
-            group_barrier(gctr, 4u * ++n_sync, lane);
+            lost |= group_barrier(gctr, 4u * ++n_sync, lane, a.spin_limit);
     };
 
     PrefillBlock B;
@@ -952,7 +1005,7 @@ __device__ __forceinline__ void prefill_body_f8(const AttnArgs &a, int bx, uint8
     auto mine = [&](int k) { return t_begin + grp + KG * k; };
     auto has = [&](int k) { return mine(k) < t_end; };
     if constexpr (KG == 2) {
-        if (tid < 2)
+        if (tid < 3)
             ((uint32_t *)(lds + KG * 2 * (2 * TN * 256)))[tid] = 0;
     }
 
@@ -1199,7 +1252,9 @@ __device__ __forceinline__ void prefill_body_f8(const AttnArgs &a, int bx, uint8
         write_rows<F16, SPLIT, 4>(a, st.o, 0, st.m, l_row, *a.v_scale, tok, head, split, lane, true);
     } else {
         const float l_row = xhalf_sum(st.l);
+        mark_lost(lost_flag, lost, lane);
         __syncthreads();
+        const bool wg_lost = __hip_atomic_load(lost_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0;
         float *rec = (float *)lds + wave * (kDecodeMergeRows * 64);
         if (grp == 1) {
 #pragma unroll
@@ -1225,6 +1280,10 @@ __device__ __forceinline__ void prefill_body_f8(const AttnArgs &a, int bx, uint8
                 st.o[x][i] = s0 * st.o[x][i] + s1 * rec[(16 * x + i) * 64 + lane];
         if (!row_ok)
             return;
+        if (wg_lost) {
+            poison_row<SPLIT>(a, tok, head, split, lane);
+            return;
+        }
         write_rows<F16, SPLIT, 4>(a, st.o, 0, M, L, *a.v_scale, tok, head, split, lane, true);
     }
 }
@@ -1473,23 +1532,32 @@ void attn_fwd_kernel(const AttnArgs a) {
 
 // One wave per row.  Lane = (split group sg = lane / 16, d chunk c = lane % 16,
 // d 8c .. 8c+7): each lane accumulates the splits p = sg, sg + 4, ..., and the
-// four split groups are summed with two cross-lane exchanges.
+// four split groups are summed with two cross-lane exchanges.  tok_end
+// (device, optional): rows of tokens at or past *tok_end belong to no
+// sequence; their partials were never written and they are skipped.  The
+// running maximum propagates NaN (a split whose key-group barrier timed out
+// stores NaN), so such a row's output is NaN rather than a plausible value.
+__device__ __forceinline__ float nan_max(float m, float x) { return (x > m || x != x) ? x : m; }
+
 template <bool F16>
 __global__ __launch_bounds__(256) void combine_kernel(const float *o_part, const float *lse_part,
                                                       int32_t P, int64_t rows, int32_t Hq, void *out,
                                                       int64_t o_st_tok, int64_t o_st_head,
-                                                      float *lse_out) {
+                                                      float *lse_out, const int32_t *tok_end) {
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= rows)
+        return;
+    const int64_t tok = row / Hq;
+    if (tok_end != nullptr && tok >= (int64_t)*tok_end)
         return;
     const int lane = threadIdx.x & 63;
     const int sg = lane >> 4;
     const int c = lane & 15;
     float L = neg_inf();
     for (int p = sg; p < P; p += 4)
-        L = fmaxf(L, lse_part[(int64_t)p * rows + row]);
-    L = fmaxf(L, __shfl_xor(L, 16));
-    L = fmaxf(L, __shfl_xor(L, 32));
+        L = nan_max(L, lse_part[(int64_t)p * rows + row]);
+    L = nan_max(L, __shfl_xor(L, 16));
+    L = nan_max(L, __shfl_xor(L, 32));
     f32x4 a0 = {0.0f, 0.0f, 0.0f, 0.0f}, a1 = a0;
     float wsum = 0.0f;
     if (L != neg_inf()) {
@@ -1514,20 +1582,23 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *o_part, const
     }
     if (sg != 0)
         return;
-    const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
-    const int64_t tok = row / Hq;
+    // wsum > 0 is false for NaN as well: a NaN row keeps its NaN sums
+    const float inv = wsum > 0.0f ? 1.0f / wsum : (wsum == 0.0f ? 0.0f : wsum);
     const int64_t head = row - tok * Hq;
     uint8_t *op = (uint8_t *)out + (tok * o_st_tok + head * o_st_head + 8 * c) * 2;
     *(u32x4 *)op = u32x4{pack2<F16>(a0[0] * inv, a0[1] * inv), pack2<F16>(a0[2] * inv, a0[3] * inv),
                          pack2<F16>(a1[0] * inv, a1[1] * inv), pack2<F16>(a1[2] * inv, a1[3] * inv)};
     if (lse_out != nullptr && c == 0)
-        lse_out[row] = wsum > 0.0f ? L + __logf(wsum) : neg_inf();
+        lse_out[row] = wsum > 0.0f ? L + __logf(wsum) : (wsum == 0.0f ? neg_inf() : wsum);
 }
 
 // ------------------------------------------------------------------ launchers
 
+// Launch status: the error state is cleared first, so that an error left by
+// an earlier call of the caller's is not reported as this launch's.
 template <bool F16, bool FP8KV, bool CAUSAL, bool SPLIT, int KG, bool EXT, bool F8MM = false>
 hipError_t launch_kernel(const AttnArgs &a, dim3 grid, hipStream_t st) {
+    (void)hipGetLastError();
     hipLaunchKernelGGL((attn_fwd_kernel<F16, FP8KV, CAUSAL, SPLIT, KG, EXT, F8MM>), grid,
                        dim3(kWaves * KG * 64), 0, st, a);
     return hipGetLastError();
@@ -1576,14 +1647,16 @@ hipError_t launch_attention(const AttnArgs &a, bool q_f16, bool kv_fp8, bool cau
 
 hipError_t launch_combine(const float *o_part, const float *lse_part, int32_t num_splits,
                           int64_t rows, int32_t num_q_heads, void *out, bool out_f16,
-                          int64_t o_st_tok, int64_t o_st_head, float *lse_out, hipStream_t stream) {
+                          int64_t o_st_tok, int64_t o_st_head, float *lse_out, const int32_t *tok_end,
+                          hipStream_t stream) {
     const dim3 grid((unsigned)((rows + 3) / 4));
+    (void)hipGetLastError();
     if (out_f16)
         hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(256), 0, stream, o_part, lse_part,
-                           num_splits, rows, num_q_heads, out, o_st_tok, o_st_head, lse_out);
+                           num_splits, rows, num_q_heads, out, o_st_tok, o_st_head, lse_out, tok_end);
     else
         hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(256), 0, stream, o_part, lse_part,
-                           num_splits, rows, num_q_heads, out, o_st_tok, o_st_head, lse_out);
+                           num_splits, rows, num_q_heads, out, o_st_tok, o_st_head, lse_out, tok_end);
     return hipGetLastError();
 }
 

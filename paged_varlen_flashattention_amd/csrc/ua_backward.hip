@@ -571,6 +571,7 @@ template <bool F16, bool CAUSAL>
 hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
     const int64_t rows = (int64_t)a.num_tokens * a.num_q_heads;
     hipError_t e = hipSuccess;
+    (void)hipGetLastError();                    // report these launches' status only
     if (rows > 0) {
         hipLaunchKernelGGL((bwd_prep_kernel<F16>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, st, a);
         if ((e = hipGetLastError()) != hipSuccess)

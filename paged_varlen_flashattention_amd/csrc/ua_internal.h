@@ -43,6 +43,7 @@ struct AttnArgs {
     int32_t win_left, win_right;   // local attention bounds (< 0: unbounded)
     const float *alibi;            // [Hq] ALiBi slopes, or null
     int32_t fp8_compute;           // fp8 caches: prefill rows use fp8 MFMA (Q, P rounded to e4m3)
+    int32_t spin_limit;            // polls per key-group barrier before it gives up (outputs NaN)
 };
 
 constexpr int kPrefillBlockM = 128;   // query rows per prefill workgroup
@@ -58,11 +59,13 @@ constexpr int kWaves = 4;             // wavefronts per workgroup, both bodies
 hipError_t launch_attention(const AttnArgs &a, bool q_f16, bool kv_fp8, bool causal, bool split,
                             bool wide, dim3 grid, hipStream_t stream);
 
-// Enqueue the split combine kernel over rows = T * Hq rows.
+// Enqueue the split combine kernel over rows = T * Hq rows.  tok_end:
+// optional device pointer to the token count that sequences cover
+// (cu_seqlens_q[S]); rows of later tokens are left untouched.
 hipError_t launch_combine(const float *o_part, const float *lse_part, int32_t num_splits,
                           int64_t rows, int32_t num_q_heads, void *out, bool out_f16,
                           int64_t o_st_tok, int64_t o_st_head, float *lse_out,
-                          hipStream_t stream);
+                          const int32_t *tok_end, hipStream_t stream);
 
 // Arguments of the KV-cache append kernel.
 struct AppendArgs {

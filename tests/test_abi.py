@@ -175,7 +175,8 @@ def test_plan_split_prefill_is_wide(lib):
     ("window_right", -5, B.UA_ERR_INVALID_ARG),
     ("alibi_slopes", FAKE + 2, B.UA_ERR_INVALID_ARG),   # not 4-byte aligned
     ("fp8_compute", 2, B.UA_ERR_INVALID_ARG),
-    ("reserved0", 1, B.UA_ERR_INVALID_ARG),
+    ("test_barrier_timeout", 2, B.UA_ERR_INVALID_ARG),
+    ("test_barrier_timeout", -1, B.UA_ERR_INVALID_ARG),
     ("fp8_compute", 1, B.UA_ERR_UNSUPPORTED),           # bf16 cache
 ])
 def test_invalid_arguments(lib, field, value, status):
@@ -193,7 +194,7 @@ def test_params_init_defaults(lib):
     lib.ua_attn_params_init(ctypes.byref(p))
     assert p.abi_version == B.ABI_VERSION and p.num_splits == 1
     assert (p.window_left, p.window_right) == (-1, -1)
-    assert not p.alibi_slopes and not p.q and p.fp8_compute == 0 and p.reserved0 == 0
+    assert not p.alibi_slopes and not p.q and p.fp8_compute == 0 and p.test_barrier_timeout == 0
     lib.ua_attn_params_init(None)                           # no-op
 
 
@@ -432,3 +433,4 @@ def test_bwd_empty_is_noop(lib):
     assert lib.ua_attention_backward(ctypes.byref(bwd_params(num_seqs=0)), None) == B.UA_OK
     assert lib.ua_attention_backward(ctypes.byref(bwd_params(num_tokens=0, num_tokens_k=0)), None) == B.UA_OK
     assert lib.ua_attention_backward(None, None) == B.UA_ERR_INVALID_ARG
+

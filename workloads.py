@@ -495,3 +495,46 @@ def backward_bench(batch: int = 4, heads: int = 32, seq: int = 4096) -> dict:
     """The page's backward benchmark (fused-attention, bwd, causal): batch 4,
     32 heads, N 4096, fp16, N(0,1) inputs, scale 1.3; head size 128."""
     return backward_case(8, [seq] * batch, [seq] * batch, heads, heads, "fp16", softmax_scale=1.3)
+
+
+def fp8_weight_pin_case(q_len: int = 40) -> Workload:
+    """A designed batch for the e4m3 rounding of the softmax weights in the
+    fp8-compute mode: one sequence of q_len queries (one head, so every row is
+    a prefill row once q_len > 32) against 64 keys in an e4m3 cache (one tile).
+
+    Inputs only: every query row is all +1 (even tokens) or all -1 (odd
+    tokens); key 0 is all zeros and key j (1..63) holds -A_j at d 0 and -B_j at
+    d 1, with A_j + B_j = n_j, n_j running over 1..71 without multiples of 8
+    (A_j, B_j exact e4m3 values); value j (1..63) is one-hot at d = j, value 0
+    is zero.  k_scale = v_scale = 1 and softmax_scale = float32(ln 2 / 8) /
+    (448 * float32(1 / 448)): with the row's e4m3 query codes (all +-448 under
+    the row scale 1/448), a +1 row's score of key j is -n_j * ln2 / 8, so its
+    weights relative to the maximum (key 0) are 2^(-n_j / 8); a -1 row's are
+    2^((n_j - 71) / 8)."""
+    n = [x for x in range(1, 72) if x % 8 != 0]
+    assert len(n) == 63
+    D = 128
+    q = torch.ones(q_len, 1, D, dtype=torch.float32)
+    q[1::2] = -1.0
+    k = torch.zeros(4, 16, 1, D, dtype=torch.float32)
+    v = torch.zeros(4, 16, 1, D, dtype=torch.float32)
+    e4m3_ints = [float(x) for x in range(0, 17)] + [float(x) for x in range(18, 33, 2)] + \
+        [float(x) for x in range(36, 65, 4)] + [float(x) for x in range(72, 129, 8)]
+    bt = [2, 0, 3, 1]                      # logical page p lives in physical block bt[p]
+    for j, nj in enumerate(n, start=1):
+        a = max(x for x in e4m3_ints if x <= nj and nj - x in e4m3_ints)
+        k[bt[j // 16], j % 16, 0, 0] = -a
+        k[bt[j // 16], j % 16, 0, 1] = -(nj - a)
+        v[bt[j // 16], j % 16, 0, j] = 1.0
+    kc = k.to(torch.float8_e4m3fn)
+    vc = v.to(torch.float8_e4m3fn)
+    assert torch.equal(kc.float(), k) and torch.equal(vc.float(), v), "values exact in e4m3"
+    sq = float(np.float32(1.0) / np.float32(448.0))
+    scale = float(np.float32(math.log(2.0) / 8.0 / (448.0 * sq)))
+    return Workload(
+        name="fp8_weight_pin", q=q.to(torch.bfloat16), k_cache=kc, v_cache=vc,
+        cu_seqlens_q=torch.tensor([0, q_len], dtype=torch.int32),
+        seqused_k=torch.tensor([64], dtype=torch.int32),
+        block_table=torch.tensor([bt], dtype=torch.int32),
+        softmax_scale=scale, causal=False, k_scale=1.0, v_scale=1.0,
+        meta={"n": n, "fp8_compute": True})
