@@ -55,7 +55,8 @@ typedef enum {
     UA_ERR_INVALID_ARG = -1,   /* null pointer, bad size, stride or alignment, abi mismatch */
     UA_ERR_UNSUPPORTED = -2,   /* valid but not implemented: head_size != 128, fp8 q, ... */
     UA_ERR_WORKSPACE = -3,     /* num_splits > 1 without a large enough workspace */
-    UA_ERR_HIP = -4            /* the HIP runtime refused a launch */
+    UA_ERR_HIP = -4,           /* the HIP runtime refused a launch */
+    UA_ERR_SCRATCH = -5        /* ua_unified_attention_noalloc: partials exceed its scratch */
 } ua_status;
 
 typedef enum {
@@ -242,6 +243,29 @@ ua_status ua_split_kv_combine(const float *o_partial, const float *lse_partial,
  * Returns 0 when num_splits <= 1. */
 size_t ua_workspace_size(int32_t num_tokens, int32_t num_q_heads, int32_t head_size,
                          int32_t num_splits);
+
+/*
+ * ua_unified_attention for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  The same computation and kernels, with the split partials in
+ * the library's own scratch array instead of a caller workspace: one array of
+ * UA_NOALLOC_SCRATCH_BYTES per GPU the library runs on, held until the
+ * process ends.  p->workspace and p->workspace_bytes are ignored; automatic
+ * splits (num_splits = 0) are chosen within the scratch.  The call allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine); its first
+ * split call on a device looks up that device's array address.
+ *
+ * Errors: as ua_unified_attention, plus UA_ERR_SCRATCH when the requested
+ * splits need more than UA_NOALLOC_SCRATCH_BYTES
+ * (ua_workspace_size(T, Hq, D, splits) > UA_NOALLOC_SCRATCH_BYTES); nothing
+ * is enqueued then.
+ *
+ * Calls that overlap on one GPU (on different streams, or from different
+ * threads without ordering) share its array and race: order them.  The array
+ * keeps the last call's partials; nothing in it needs to start at zero.
+ */
+#define UA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+ua_status ua_unified_attention_noalloc(const ua_attn_params *p, void *stream);
 
 /* The launch ua_unified_attention would make for *p (host only, no HIP call).
  * Validates *p exactly as ua_unified_attention does. */

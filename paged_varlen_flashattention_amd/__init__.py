@@ -11,11 +11,13 @@ from ._binding import (ABI_VERSION, EXPORTS, LIB_PATH, UA_BF16, UA_ERR_HIP, UA_E
                        AppendParams, AttnParams, BwdParams, PlanInfo, UAError, attention_backward,
                        auto_splits, bwd_workspace_size, kv_append, make_bwd_params,
                        load_library, make_append_params, make_params, plan,
-                       split_kv_combine, status_string, unified_attention, workspace_size)
+                       split_kv_combine, status_string, unified_attention, workspace_size,
+                       UA_ERR_SCRATCH, NOALLOC_SCRATCH_BYTES, unified_attention_noalloc)
 
 __all__ = ["ABI_VERSION", "EXPORTS", "LIB_PATH", "AppendParams", "AttnParams", "BwdParams", "PlanInfo",
            "attention_backward", "bwd_workspace_size", "make_bwd_params",
            "UAError", "auto_splits", "kv_append", "make_append_params", "load_library", "make_params", "plan", "split_kv_combine", "status_string",
-           "unified_attention", "workspace_size", "UA_OK", "UA_ERR_INVALID_ARG",
+           "unified_attention", "unified_attention_noalloc", "workspace_size", "UA_OK",
+           "UA_ERR_SCRATCH", "NOALLOC_SCRATCH_BYTES", "UA_ERR_INVALID_ARG",
            "UA_ERR_UNSUPPORTED", "UA_ERR_WORKSPACE", "UA_ERR_HIP", "UA_BF16", "UA_FP16",
            "UA_FP8_E4M3FN"]

@@ -18,6 +18,8 @@ LIB_PATH = os.path.join(HERE, "libua.so")
 ABI_VERSION = 4
 
 UA_OK, UA_ERR_INVALID_ARG, UA_ERR_UNSUPPORTED, UA_ERR_WORKSPACE, UA_ERR_HIP = 0, -1, -2, -3, -4
+UA_ERR_SCRATCH = -5
+NOALLOC_SCRATCH_BYTES = 64 << 20      # UA_NOALLOC_SCRATCH_BYTES
 UA_BF16, UA_FP16, UA_FP8_E4M3FN = 0, 1, 2
 _DTYPES = {torch.bfloat16: UA_BF16, torch.float16: UA_FP16, torch.float8_e4m3fn: UA_FP8_E4M3FN}
 
@@ -25,7 +27,8 @@ _DTYPES = {torch.bfloat16: UA_BF16, torch.float16: UA_FP16, torch.float8_e4m3fn:
 EXPORTS = ("ua_unified_attention", "ua_split_kv_combine", "ua_workspace_size", "ua_plan",
            "ua_status_string", "ua_abi_version", "ua_params_size", "ua_plan_info_size",
            "ua_kv_append", "ua_append_params_size", "ua_attn_params_init",
-           "ua_attention_backward", "ua_bwd_workspace_size", "ua_bwd_params_size")
+           "ua_attention_backward", "ua_bwd_workspace_size", "ua_bwd_params_size",
+           "ua_unified_attention_noalloc")
 
 
 class UAError(RuntimeError):
@@ -123,6 +126,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     lib.ua_unified_attention.argtypes = [ctypes.POINTER(AttnParams), vp]
     lib.ua_unified_attention.restype = ctypes.c_int
+    lib.ua_unified_attention_noalloc.argtypes = [ctypes.POINTER(AttnParams), vp]
+    lib.ua_unified_attention_noalloc.restype = ctypes.c_int
     lib.ua_split_kv_combine.argtypes = [vp, vp, i32, i32, i32, i32, vp, i32, i64, i64, vp, vp]
     lib.ua_split_kv_combine.restype = ctypes.c_int
     lib.ua_workspace_size.argtypes = [i32, i32, i32, i32]
@@ -276,6 +281,22 @@ def unified_attention(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_t
     st = load_library().ua_unified_attention(ctypes.byref(p), _stream_handle(stream))
     if st != UA_OK:
         raise UAError(st, "ua_unified_attention")
+    return out
+
+
+def unified_attention_noalloc(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table,
+                              max_seqlen_q, max_seqlen_k, softmax_scale, causal, k_scale=None,
+                              v_scale=None, num_splits=1, lse=None, stream=None, window=(-1, -1),
+                              alibi_slopes=None, fp8_compute=False):
+    """ua_unified_attention_noalloc on torch device tensors: as
+    unified_attention, with the split partials in the library's per-device
+    scratch (nothing is allocated, here or in the library)."""
+    p = make_params(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table, max_seqlen_q,
+                    max_seqlen_k, softmax_scale, causal, k_scale, v_scale, num_splits, lse, None,
+                    window, alibi_slopes, fp8_compute)
+    st = load_library().ua_unified_attention_noalloc(ctypes.byref(p), _stream_handle(stream))
+    if st != UA_OK:
+        raise UAError(st, "ua_unified_attention_noalloc")
     return out
 
 

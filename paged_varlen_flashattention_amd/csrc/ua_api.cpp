@@ -345,6 +345,8 @@ const char *ua_status_string(int32_t status) {
     case UA_ERR_UNSUPPORTED: return "unsupported configuration";
     case UA_ERR_WORKSPACE: return "workspace missing or too small for the requested splits";
     case UA_ERR_HIP: return "HIP runtime error";
+    case UA_ERR_SCRATCH:
+        return "the requested splits need more than the no-allocation scratch (UA_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
     }
 }
@@ -457,6 +459,36 @@ ua_status ua_unified_attention(const ua_attn_params *p, void *stream) {
             return UA_ERR_HIP;
     }
     return UA_OK;
+}
+
+ua_status ua_unified_attention_noalloc(const ua_attn_params *p, void *stream) {
+    if (p == nullptr)
+        return UA_ERR_INVALID_ARG;
+    // validate and plan against the scratch's size before any HIP call (an
+    // aligned stand-in address until a split needs the real one)
+    ua_attn_params q = *p;
+    q.workspace = reinterpret_cast<void *>(kAlign);
+    q.workspace_bytes = UA_NOALLOC_SCRATCH_BYTES;
+    ua_plan_info info;
+    const ua_status st = ua_plan(&q, &info);
+    if (st == UA_ERR_WORKSPACE)
+        return UA_ERR_SCRATCH;
+    if (st != UA_OK)
+        return st;
+    if (p->num_seqs == 0 || p->num_tokens == 0)
+        return UA_OK;
+    if (info.num_splits > 1) {
+        void *ptr = nullptr;
+        if (ua::noalloc_scratch(&ptr) != hipSuccess)
+            return UA_ERR_HIP;
+        q.workspace = ptr;
+        q.num_splits = info.num_splits;
+    } else {
+        q.workspace = nullptr;
+        q.workspace_bytes = 0;
+        q.num_splits = 1;
+    }
+    return ua_unified_attention(&q, stream);
 }
 
 ua_status ua_split_kv_combine(const float *o_partial, const float *lse_partial, int32_t num_splits,

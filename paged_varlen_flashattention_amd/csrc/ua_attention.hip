@@ -50,11 +50,13 @@
 // of key tiles and stores a normalised fp32 partial and its natural-log
 // log-sum-exp; combine_kernel merges them.
 
+#include "ua.h"
 #include "ua_internal.h"
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 namespace ua {
@@ -1643,6 +1645,40 @@ hipError_t launch_attention(const AttnArgs &a, bool q_f16, bool kv_fp8, bool cau
                       : launch_mode<true, false>(a, causal, split, wide, ext, grid, stream);
     return kv_fp8 ? launch_mode<false, true>(a, causal, split, wide, ext, grid, stream)
                   : launch_mode<false, false>(a, causal, split, wide, ext, grid, stream);
+}
+
+// ------------------------------------------------------------------ no-allocation scratch
+
+// Split partials of ua_unified_attention_noalloc: one array per GPU, held
+// until the process ends.  Host code never uses the array's name as an
+// address (on the host it is a stand-in, not device memory): the device
+// address comes from hipGetSymbolAddress, once per device with that device
+// current, and is kept per device.
+static __device__ __align__(256) uint8_t scratch[UA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t noalloc_scratch(void **ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_combine(const float *o_part, const float *lse_part, int32_t num_splits,

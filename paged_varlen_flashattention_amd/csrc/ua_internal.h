@@ -67,6 +67,10 @@ hipError_t launch_combine(const float *o_part, const float *lse_part, int32_t nu
                           int64_t o_st_tok, int64_t o_st_head, float *lse_out,
                           const int32_t *tok_end, hipStream_t stream);
 
+// Device address of this GPU's no-allocation scratch array
+// (UA_NOALLOC_SCRATCH_BYTES bytes, 256-byte aligned), looked up once per device.
+hipError_t noalloc_scratch(void **ptr);
+
 // Arguments of the KV-cache append kernel.
 struct AppendArgs {
     const void *k_new;

@@ -434,3 +434,30 @@ def test_bwd_empty_is_noop(lib):
     assert lib.ua_attention_backward(ctypes.byref(bwd_params(num_tokens=0, num_tokens_k=0)), None) == B.UA_OK
     assert lib.ua_attention_backward(None, None) == B.UA_ERR_INVALID_ARG
 
+
+# ------------------------------------------------------------------ no-allocation entry point
+
+def test_noalloc_rejects_splits_beyond_its_scratch(lib):
+    # 256 rows x 32 heads: 128 splits need 128 * 256 * 32 * 129 * 4 B > 64 MiB
+    p = base_params(num_splits=128)
+    need = lib.ua_workspace_size(p.num_tokens, p.num_q_heads, 128, 128)
+    assert need > B.NOALLOC_SCRATCH_BYTES
+    assert lib.ua_unified_attention_noalloc(ctypes.byref(p), None) == B.UA_ERR_SCRATCH
+    assert "scratch" in ua.status_string(B.UA_ERR_SCRATCH)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("abi_version", 3, B.UA_ERR_INVALID_ARG),
+    ("head_size", 64, B.UA_ERR_UNSUPPORTED),
+    ("q", 0, B.UA_ERR_INVALID_ARG),
+    ("num_splits", 129, B.UA_ERR_INVALID_ARG),
+])
+def test_noalloc_validates_like_the_workspace_entry(lib, field, value, status):
+    p = base_params(**{field: value})
+    assert lib.ua_unified_attention_noalloc(ctypes.byref(p), None) == status
+    assert lib.ua_unified_attention_noalloc(None, None) == B.UA_ERR_INVALID_ARG
+
+
+def test_noalloc_no_op_batches(lib):
+    for kw in ({"num_seqs": 0}, {"num_tokens": 0}):
+        assert lib.ua_unified_attention_noalloc(ctypes.byref(base_params(**kw)), None) == B.UA_OK
