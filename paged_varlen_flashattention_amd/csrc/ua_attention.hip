@@ -189,6 +189,21 @@ __device__ __forceinline__ void lds_dma16(const uint8_t *base, uint32_t lane_ofs
                  : "memory", "m0");
 }
 
+// As lds_dma16, with the LDS row given as a wave-uniform base plus a
+// compile-time byte offset added in the same asm block (s_add_u32 m0), so the
+// compiler keeps one scalar base instead of one register per row address (the
+// 16 row addresses of a tile's loads otherwise spill to VGPR lanes and are
+// reloaded every tile).  s_add_u32 writes SCC, hence the "scc" clobber: the
+// compiler must not keep a carry (the high half of a 64-bit add) or a branch
+// condition live across this block.
+template <int OFS>
+__device__ __forceinline__ void lds_dma16_at(const uint8_t *base, uint32_t lane_ofs, uint32_t lds_base) {
+    asm volatile("s_add_u32 m0, %2, %3\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(lane_ofs), "s"(base), "s"(lds_base), "i"(OFS)
+                 : "memory", "m0", "scc");
+}
+
 // Combine a value with the one held by the lane 32 positions away (the other
 // half of the wave), on every lane: v_permlane32_swap exchanges the halves of
 // two registers, so with both operands equal to v the two results hold v and
@@ -721,29 +736,43 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, int bx, uint8_t 
         // swizzled position that is.  The DMA of tile + 1 runs under the
         // compute of tile; one barrier per tile.  The page id is a scalar load
         // fetched a tile ahead.
+        // per-lane global offsets of the four 4-key instructions per tensor
+        // (the row group included, so all four share the page's scalar
+        // base); m0 of each instruction is the wave's first row in the
+        // group's LDS area plus a compile-time offset
         const int lrow = lane >> 4;                           // row within a 4-key group
-        const uint32_t rofs = (uint32_t)(lrow * a.kv_st_slot * KVB);
-        uint32_t koff[4];
+        uint32_t koff[4], voff[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t rofs = (uint32_t)((4 * i + lrow) * a.kv_st_slot * KVB);
             koff[i] = rofs + (uint32_t)(((lane & 15) ^ swz_k(4 * i + lrow)) << 4);
-        const uint32_t voff = rofs + (uint32_t)(((lane & 15) ^ swz_v(lrow)) << 4);
+            voff[i] = rofs + (uint32_t)(((lane & 15) ^ swz_v(lrow)) << 4);
+        }
         const int wrow = 16 * wv;                             // this wave's first key in the tile
+        const uint32_t lds_row0 = (uint32_t)reinterpret_cast<uintptr_t>(
+            (__attribute__((address_space(3))) uint8_t *)(sK0)) + (uint32_t)(wrow * 256);
         int32_t blk = 0;
         auto fetch_id = [&](int tile) {
             blk = sload(btrow + min((tile * TN + wrow) >> lbs, last_page));
         };
-        auto dma_tile = [&](int tile, uint8_t *sK, uint8_t *sV) {
+        // STG: 0 fills the first K/V stage of the group, 1 the second
+        auto dma_tile = [&](int tile, auto stg) {
+            constexpr int KOFS = decltype(stg)::value * STAGE, VOFS = KOFS + TN * 256;
             const int j = tile * TN + wrow;
             const int64_t pofs =
                 ((int64_t)blk * a.kv_st_blk + (int64_t)(j & bs_mask) * a.kv_st_slot) * KVB;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t gofs = pofs + (int64_t)(4 * i) * a.kv_st_slot * KVB;
-                lds_dma16(kbase + gofs, koff[i], sK + (wrow + 4 * i) * 256);
-                lds_dma16(vbase + gofs, voff, sV + (wrow + 4 * i) * 256);
-            }
+            const uint8_t *gk = kbase + pofs, *gv = vbase + pofs;
+            lds_dma16_at<KOFS + 0 * 256>(gk, koff[0], lds_row0);
+            lds_dma16_at<VOFS + 0 * 256>(gv, voff[0], lds_row0);
+            lds_dma16_at<KOFS + 4 * 256>(gk, koff[1], lds_row0);
+            lds_dma16_at<VOFS + 4 * 256>(gv, voff[1], lds_row0);
+            lds_dma16_at<KOFS + 8 * 256>(gk, koff[2], lds_row0);
+            lds_dma16_at<VOFS + 8 * 256>(gv, voff[2], lds_row0);
+            lds_dma16_at<KOFS + 12 * 256>(gk, koff[3], lds_row0);
+            lds_dma16_at<VOFS + 12 * 256>(gv, voff[3], lds_row0);
         };
+        using Stg0 = std::integral_constant<int, 0>;
+        using Stg1 = std::integral_constant<int, 1>;
         // keys at or past kv_end came from a clamped (allocated) page: zero
         // their V rows so that weight 0 times whatever was there stays 0
         auto zero_tail = [&](int tile, uint8_t *sV) {
@@ -757,7 +786,7 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, int bx, uint8_t 
         if (n_it > 0) {
             if (has(0)) {
                 fetch_id(mine(0));
-                dma_tile(mine(0), sK0, sV0);
+                dma_tile(mine(0), Stg0{});
                 if (has(1))
                     fetch_id(mine(1));
             }
@@ -767,9 +796,9 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, int bx, uint8_t 
             __syncthreads();
         }
         // unrolled by two so that each stage's LDS addresses are constants
-        auto step = [&](int k, uint8_t *cK, uint8_t *cV, uint8_t *nK, uint8_t *nV) {
+        auto step = [&](int k, uint8_t *cK, uint8_t *cV, auto nstg, uint8_t *nV) {
             if (has(k + 1)) {
-                dma_tile(mine(k + 1), nK, nV);
+                dma_tile(mine(k + 1), nstg);
                 if (has(k + 2))
                     fetch_id(mine(k + 2));
             }
@@ -783,9 +812,9 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, int bx, uint8_t 
             }
         };
         for (int k = 0; k < n_it; k += 2) {
-            step(k, sK0, sV0, sK1, sV1);
+            step(k, sK0, sV0, Stg1{}, sV1);
             if (k + 1 < n_it)
-                step(k + 1, sK1, sV1, sK0, sV0);
+                step(k + 1, sK1, sV1, Stg0{}, sV0);
         }
     } else {
         // fp8 caches: codes are loaded into registers two tiles ahead (two
