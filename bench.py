@@ -161,7 +161,16 @@ def build_calls(cfg: str, splits_override):
             s = splits_override
         return (f"decode_paged_gqa_256seq_32q8kv_bs16_splits{s}", [("decode", wl, s)])
     if cfg == "c4":
-        return ("mixed_chunked_prefill_64dec_4x2048_64q8kv_bs32", [("mixed", wk.config4(), 1)])
+        wl = wk.config4()
+        if splits_override is None:
+            # the planner's choice: the decode rows split (-n), prefill rows not
+            import paged_varlen_flashattention_amd as ua
+            s = ua.auto_splits(wl.q, wl.k_cache, wl.v_cache, wl.q, wl.cu_seqlens_q, wl.seqused_k,
+                               wl.block_table, wl.max_seqlen_q, wl.max_seqlen_k, wl.softmax_scale,
+                               wl.causal)
+        else:
+            s = splits_override
+        return (f"mixed_chunked_prefill_64dec_4x2048_64q8kv_bs32_splits{s}", [("mixed", wl, s)])
     s = 32 if splits_override is None else splits_override
     return (f"long_ctx_fp8kv_2x131072_64q8kv_splits{s}", [("long", wk.config5(), s)])
 
@@ -211,8 +220,8 @@ def main():
         }
         d["out"] = torch.empty_like(d["q"])
         ws = None
-        if splits > 1:
-            ws = torch.empty(ua.workspace_size(wl.num_tokens, wl.num_q_heads, 128, splits),
+        if abs(splits) > 1:
+            ws = torch.empty(ua.workspace_size(wl.num_tokens, wl.num_q_heads, 128, abs(splits)),
                              dtype=torch.uint8, device=dev)
         prepared.append((label, wl, splits, d, ws))
     stream = torch.cuda.current_stream()
@@ -336,8 +345,8 @@ def decode_half(args, call, stream) -> dict:
              "alibi": None, "window": (-1, -1), "f8": False}
         d["out"] = torch.empty_like(d["q"])
         ws = None
-        if splits > 1:
-            ws = torch.empty(ua.workspace_size(wl.num_tokens, wl.num_q_heads, 128, splits),
+        if abs(splits) > 1:
+            ws = torch.empty(ua.workspace_size(wl.num_tokens, wl.num_q_heads, 128, abs(splits)),
                              dtype=torch.uint8, device=dev)
         fn = lambda: call(wl, splits, d, ws)
         for _ in range(args.warmup):
@@ -642,8 +651,8 @@ def extras(args, prepared, per, result, call, stream) -> None:
         d["out"] = torch.empty_like(d["q"])
         import paged_varlen_flashattention_amd as ua
         ws = None
-        if splits > 1:
-            ws = torch.empty(ua.workspace_size(wl.num_tokens, wl.num_q_heads, 128, splits),
+        if abs(splits) > 1:
+            ws = torch.empty(ua.workspace_size(wl.num_tokens, wl.num_q_heads, 128, abs(splits)),
                              dtype=torch.uint8, device=dev)
         fn = lambda: call(wl, splits, d, ws)
         for _ in range(3):
@@ -684,19 +693,29 @@ def extras(args, prepared, per, result, call, stream) -> None:
         ql = wl.q_lens
         dec = wk.subset(wl, [s for s in range(len(ql)) if ql[s] == 1], "c4_decode_part")
         pre = wk.subset(wl, [s for s in range(len(ql)) if ql[s] > 1], "c4_prefill_part")
+        # the decode part alone unsplit and with the launch's decode split,
+        # the prefill part alone, and the whole batch with no split at all
+        ds = abs(prepared[0][2])
         med_d, _ = run_sub(dec, 1)
+        med_ds, _ = run_sub(dec, ds) if ds > 1 else (med_d, None)
         med_p, _ = run_sub(pre, 1)
+        med_u, _ = run_sub(wl, 1)
         t_mfma = wl.flops() / (PEAK_MFMA_TFLOPS * 1e12) * 1e6
         t_hbm = wl.kv_bytes() / (PEAK_HBM_GBS * 1e9) * 1e6
         t_roof = max(t_mfma, t_hbm)
         meas = per[prepared[0][0]]["ms_median"] * 1e3
+        gbs = lambda ms: dec.kv_bytes() / (ms * 1e-3) / 1e9
         result["sub_batches"] = {
-            "decode_only": {"ms_median": round(med_d, 4),
-                            "GB/s": round(dec.kv_bytes() / (med_d * 1e-3) / 1e9, 1),
-                            "hbm_frac": round(dec.kv_bytes() / (med_d * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+            "decode_only": {"splits": 1, "ms_median": round(med_d, 4), "GB/s": round(gbs(med_d), 1),
+                            "hbm_frac": round(gbs(med_d) / PEAK_HBM_GBS, 4)},
+            "decode_only_split": {"splits": ds, "ms_median": round(med_ds, 4),
+                                  "GB/s": round(gbs(med_ds), 1),
+                                  "hbm_frac": round(gbs(med_ds) / PEAK_HBM_GBS, 4)},
             "prefill_only": {"ms_median": round(med_p, 4),
                              "TFLOP/s": round(pre.flops() / (med_p * 1e-3) / 1e12, 1),
                              "mfma_frac": round(pre.flops() / (med_p * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4)},
+            "whole_unsplit": {"ms_median": round(med_u, 4),
+                              "TFLOP/s": round(wl.flops() / (med_u * 1e-3) / 1e12, 1)},
             "t_roof_us": round(t_roof, 1), "t_roof_mfma_us": round(t_mfma, 1),
             "t_roof_hbm_us": round(t_hbm, 1), "measured_us": round(meas, 1),
             "frac_of_roof": round(t_roof / meas, 4)}

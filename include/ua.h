@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define UA_ABI_VERSION 4u
+#define UA_ABI_VERSION 5u
 
 typedef enum {
     UA_OK = 0,
@@ -129,7 +129,13 @@ typedef enum {
  * num_splits   0 = choose automatically, 1 = no split, 2..128 = split each
  *              query block's key range into that many contiguous chunks whose
  *              partials (fp32 output + log-sum-exp) are merged by the combine
- *              kernel on the same stream.
+ *              kernel on the same stream.  -128..-2 = split only the rows of
+ *              decode sequences (q_len * Hq / Hkv <= 32) that many ways and
+ *              combine only those rows; the other rows are computed unsplit
+ *              (-1 = no split).  Automatic choice does this for a batch with
+ *              prefill work that stays unsplit and may hold decode sequences
+ *              (T - (S - 1) * max_seqlen_q <= 32 / (Hq / Hkv)): one split per
+ *              4096 keys of max_seqlen_k, at most 8.
  * workspace,   device scratch for the partials, at least
  * workspace_bytes  ua_workspace_size(T, Hq, D, splits) bytes, 256-byte
  *              aligned; may be NULL when no split is used.  Automatic split
@@ -151,7 +157,7 @@ typedef enum {
  * and T > 0); D == 128; Hq % Hkv == 0 and Hq / Hkv <= 128; bs a power of two
  * in [16, 4096]; W >= ceil(max_seqlen_k / bs); all strides multiples of 8 and
  * positive, kv_stride_slot < 2^26; q, out, k_cache, v_cache 16-byte aligned;
- * num_splits <= 128.
+ * -128 <= num_splits <= 128.
  * S == 0 or T == 0 is a no-op that returns UA_OK.
  */
 typedef struct ua_attn_params {
@@ -197,7 +203,10 @@ typedef struct ua_attn_params {
  * runs; otherwise both run and the prefill kernel skips the short sequences.
  * Split launches with prefill work use 8-wave workgroups: two groups of 4
  * prefill waves take alternate tiles of the split and merge, and the decode
- * body streams with 8 waves. */
+ * body streams with 8 waves.  A launch that splits only the decode rows
+ * (kernels bit 2) keeps 4-wave workgroups: decode_grid_x decode workgroups
+ * (sequence x kv head x split) spread among the grid_x prefill workgroups in
+ * one dimension, grid_y = 1. */
 typedef struct ua_plan_info {
     int32_t block_m;       /* query rows per prefill workgroup */
     int32_t block_q;       /* query tokens per prefill workgroup = block_m / (Hq / Hkv) */
@@ -205,10 +214,12 @@ typedef struct ua_plan_info {
     int32_t num_waves;     /* 64-lane wavefronts per workgroup (both bodies): 4, or 8 for split
                               launches with prefill work (two key groups per query block) */
     int32_t num_splits;    /* splits actually used (1 = no combine launch) */
-    int32_t kernels;       /* bit 0: prefill kernel launched; bit 1: decode kernel launched */
+    int32_t kernels;       /* bit 0: prefill kernel launched; bit 1: decode kernel launched;
+                              bit 2: only the decode rows are split (num_splits ways) */
     int64_t grid_x;        /* prefill workgroups along (query block slot x kv head); 0 if not launched */
-    int64_t grid_y;        /* workgroups along splits (both kernels) */
-    int64_t decode_grid_x; /* decode workgroups along (sequence x kv head); 0 if not launched */
+    int64_t grid_y;        /* workgroups along splits (both kernels); 1 when bit 2 is set */
+    int64_t decode_grid_x; /* decode workgroups along (sequence x kv head), times num_splits
+                              when bit 2 is set; 0 if not launched */
 } ua_plan_info;
 
 /*

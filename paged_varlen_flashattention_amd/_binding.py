@@ -15,7 +15,7 @@ import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libua.so")
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 UA_OK, UA_ERR_INVALID_ARG, UA_ERR_UNSUPPORTED, UA_ERR_WORKSPACE, UA_ERR_HIP = 0, -1, -2, -3, -4
 UA_ERR_SCRATCH = -5
@@ -240,13 +240,16 @@ def plan(params: AttnParams) -> dict:
 def auto_splits(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table, max_seqlen_q,
                 max_seqlen_k, softmax_scale, causal, k_scale=None, v_scale=None, window=(-1, -1),
                 alibi_slopes=None) -> int:
-    """The split count the planner picks for num_splits = 0 given unlimited
-    workspace (host only, no device work)."""
+    """The split the planner picks for num_splits = 0 given unlimited workspace
+    (host only, no device work), as the num_splits value that asks for it
+    explicitly: n for n splits of every row, -n when only the decode rows are
+    split n ways."""
     probe = make_params(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table,
                         max_seqlen_q, max_seqlen_k, softmax_scale, causal, k_scale, v_scale, 0,
                         None, None, window, alibi_slopes)
     probe.workspace, probe.workspace_bytes = 256, 1 << 62
-    return plan(probe)["num_splits"]
+    info = plan(probe)
+    return -info["num_splits"] if info["kernels"] & 4 else info["num_splits"]
 
 
 def unified_attention(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table,
@@ -262,12 +265,13 @@ def unified_attention(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_t
     fp8 caches; lse optional [T, Hq] fp32; window (left, right) local attention
     bounds (-1 = unbounded); alibi_slopes optional [Hq] fp32 device tensor;
     fp8_compute: with an fp8 cache, prefill rows on the fp8 matrix cores.
-    With num_splits > 1 (or 0 = auto) a
-    workspace of workspace_size(...) bytes is allocated here when none is
-    given.  Enqueued on `stream` (default: torch's current stream).
+    num_splits: 0 = auto, 1 = none, n > 1 = every row split n ways, -n =
+    only the decode sequences' rows split n ways.  With a split (or auto) a
+    workspace of workspace_size(..., |num_splits|) bytes is allocated here when
+    none is given.  Enqueued on `stream` (default: torch's current stream).
     """
-    if workspace is None and num_splits != 1:
-        splits = num_splits
+    if workspace is None and num_splits not in (1, -1):
+        splits = abs(num_splits)
         if splits == 0:
             splits = auto_splits(q, k_cache, v_cache, out, cu_seqlens_q, seqused_k, block_table,
                                  max_seqlen_q, max_seqlen_k, softmax_scale, causal, k_scale,

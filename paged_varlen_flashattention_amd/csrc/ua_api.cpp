@@ -25,6 +25,10 @@ constexpr int kMaxGroup = 128;
 constexpr size_t kAlign = 256;
 constexpr int kNumCUs = 256;
 constexpr int kBarrierPolls = 1 << 20;   // polls before a key-group barrier wait gives up
+// Automatic split of a mixed batch's decode rows: one split per this many keys
+// of the longest sequence, at most kMaxDecodeSplits.
+constexpr int kDecodeSplitKeys = 4096;
+constexpr int kMaxDecodeSplits = 8;
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 bool pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
@@ -48,7 +52,7 @@ ua_status validate(const ua_attn_params *p) {
         return UA_ERR_INVALID_ARG;
     if (p->num_seqs < 0 || p->num_tokens < 0)
         return UA_ERR_INVALID_ARG;
-    if (p->num_splits < 0 || p->num_splits > kMaxSplits)
+    if (p->num_splits < -kMaxSplits || p->num_splits > kMaxSplits)
         return UA_ERR_INVALID_ARG;
     if (p->num_seqs == 0 || p->num_tokens == 0)
         return UA_OK;                                          // nothing to do
@@ -113,7 +117,16 @@ struct Plan {
     int32_t splits;
     int64_t qslots;        // prefill query-block slots
     bool wide;             // 8-wave workgroups: two prefill key groups per query block
+    bool mix;              // only the decode rows are split (prefill rows unsplit)
 };
+
+// Whether some sequence can be a decode sequence (q_len * G <= kDecodeRows)
+// given only T, S and max_seqlen_q: the shortest sequence has at least
+// T - (S - 1) * max_seqlen_q tokens.
+bool may_have_decode_rows(const ua_attn_params *p, int G) {
+    return (int64_t)p->num_tokens - (int64_t)(p->num_seqs - 1) * p->max_seqlen_q <=
+           ua::kDecodeRows / G;
+}
 
 // Kernel choice: every sequence with q_len * G <= kDecodeRows rows goes to the
 // decode kernel; when max_seqlen_q * G <= kDecodeRows that is every sequence
@@ -124,6 +137,11 @@ struct Plan {
 // launches at about eight rounds, since their workgroups are short and
 // memory-bound and more of them balance uneven key lengths (on the 256 x
 // (1 query, 512..8192 keys) decode batch 2 splits stream best, 8 cost ~6%).
+// A launch with prefill work that stays unsplit and may hold decode sequences
+// splits only the decode rows, one split per kDecodeSplitKeys keys of the
+// longest sequence (at most kMaxDecodeSplits): its decode workgroups are then
+// short and are spread among the prefill ones instead of occupying every slot
+// at the start.  num_splits = -n asks for that decode-only split explicitly.
 Plan make_plan(const ua_attn_params *p) {
     Plan pl;
     const int G = p->num_q_heads / p->num_kv_heads;
@@ -132,7 +150,12 @@ Plan make_plan(const ua_attn_params *p) {
     pl.decode = true;
     pl.block_q = ua::kPrefillBlockM / G;
     pl.qslots = (int64_t)p->num_tokens / pl.block_q + p->num_seqs;
+    pl.mix = false;
     int splits = p->num_splits;
+    if (splits < 0) {
+        splits = -splits;
+        pl.mix = pl.prefill;            // decode-only launches: every row is a decode row
+    }
     if (splits == 0) {
         int64_t units;
         int64_t min_keys;
@@ -153,13 +176,25 @@ Plan make_plan(const ua_attn_params *p) {
         while (splits > 1 && ua_workspace_size(p->num_tokens, p->num_q_heads, p->head_size, splits) >
                                  (p->workspace ? p->workspace_bytes : 0))
             --splits;
+        if (!decode_only && splits <= 1 && may_have_decode_rows(p, G)) {
+            int ds = (int)std::min<int64_t>(kMaxDecodeSplits, p->max_seqlen_k / kDecodeSplitKeys);
+            while (ds > 1 && ua_workspace_size(p->num_tokens, p->num_q_heads, p->head_size, ds) >
+                                 (p->workspace ? p->workspace_bytes : 0))
+                --ds;
+            if (ds > 1) {
+                splits = ds;
+                pl.mix = true;
+            }
+        }
     }
     pl.splits = std::max(1, splits);
+    if (pl.splits == 1)
+        pl.mix = false;
     // A split launch with prefill work has few query blocks per kv head (that
     // is why it splits): its prefill workgroups run two key groups over
     // alternate tiles, so that one workgroup per CU still puts two waves on
     // every SIMD.
-    pl.wide = pl.prefill && pl.splits > 1;
+    pl.wide = pl.prefill && pl.splits > 1 && !pl.mix;
     return pl;
 }
 
@@ -379,10 +414,11 @@ ua_status ua_plan(const ua_attn_params *p, ua_plan_info *plan) {
     plan->tile_n = ua::kPrefillTileN;
     plan->num_waves = pl.wide ? 2 * ua::kWaves : ua::kWaves;
     plan->num_splits = pl.splits;
-    plan->kernels = (pl.prefill ? 1 : 0) | (pl.decode ? 2 : 0);
+    plan->kernels = (pl.prefill ? 1 : 0) | (pl.decode ? 2 : 0) | (pl.mix ? 4 : 0);
     plan->grid_x = pl.prefill ? pl.qslots * p->num_kv_heads : 0;
-    plan->grid_y = pl.splits;
-    plan->decode_grid_x = pl.decode ? (int64_t)p->num_seqs * p->num_kv_heads : 0;
+    plan->grid_y = pl.mix ? 1 : pl.splits;
+    plan->decode_grid_x =
+        pl.decode ? (int64_t)p->num_seqs * p->num_kv_heads * (pl.mix ? pl.splits : 1) : 0;
     return UA_OK;
 }
 
@@ -393,7 +429,7 @@ ua_status ua_unified_attention(const ua_attn_params *p, void *stream) {
         return st;
     if (p->num_seqs == 0 || p->num_tokens == 0)
         return UA_OK;
-    if (info.grid_x + info.decode_grid_x > 0x7fffffff)
+    if (info.grid_x + info.decode_grid_x > 0x7fffffff - 16)
         return UA_ERR_UNSUPPORTED;
     const Plan pl = make_plan(p);
     const bool split = pl.splits > 1;
@@ -409,7 +445,7 @@ ua_status ua_unified_attention(const ua_attn_params *p, void *stream) {
     a.block_table = p->block_table;
     a.k_scale = p->kv_dtype == UA_FP8_E4M3FN ? p->k_scale : nullptr;
     a.v_scale = p->kv_dtype == UA_FP8_E4M3FN ? p->v_scale : nullptr;
-    a.lse_out = split ? nullptr : p->lse_out;
+    a.lse_out = split && !pl.mix ? nullptr : p->lse_out;   // mixed: the prefill rows' own
     if (split) {
         uint8_t *ws = static_cast<uint8_t *>(p->workspace);
         a.o_part = reinterpret_cast<float *>(ws);
@@ -437,6 +473,15 @@ ua_status ua_unified_attention(const ua_attn_params *p, void *stream) {
     a.scale_log2 = p->softmax_scale * 1.44269504088896341f;
 
     a.decode_wgs = (int32_t)info.decode_grid_x;
+    dim3 grid((unsigned)(info.grid_x + info.decode_grid_x), (unsigned)info.grid_y);
+    if (pl.mix) {
+        // decode blocks spread over the whole grid (see the kernel's MIX entry)
+        const int64_t nd = (info.decode_grid_x + 7) / 8, np = (info.grid_x + 7) / 8;
+        a.prefill_wgs = (int32_t)info.grid_x;
+        a.mix_dblocks = (int32_t)nd;
+        a.mix_region = (int32_t)(nd + np);
+        grid = dim3((unsigned)(8 * (nd + np)), 1);
+    }
     a.win_left = p->window_left;
     a.win_right = p->window_right;
     a.alibi = p->alibi_slopes;
@@ -445,11 +490,17 @@ ua_status ua_unified_attention(const ua_attn_params *p, void *stream) {
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool f16 = p->q_dtype == UA_FP16, fp8 = p->kv_dtype == UA_FP8_E4M3FN, causal = p->causal != 0;
-    if (ua::launch_attention(a, f16, fp8, causal, split, pl.wide,
-                             dim3((unsigned)(info.grid_x + info.decode_grid_x), (unsigned)info.grid_y),
-                             s) != hipSuccess)
+    if (ua::launch_attention(a, f16, fp8, causal, split && !pl.mix, pl.wide, pl.mix, grid, s) !=
+        hipSuccess)
         return UA_ERR_HIP;
-    if (split) {
+    if (pl.mix) {
+        if (ua::launch_combine_decode(a.o_part, a.lse_part, pl.splits,
+                                      (int64_t)p->num_tokens * p->num_q_heads, p->num_q_heads,
+                                      p->num_kv_heads, p->num_seqs, p->cu_seqlens_q, p->out,
+                                      p->q_dtype == UA_FP16, p->o_stride_token, p->o_stride_head,
+                                      p->lse_out, s) != hipSuccess)
+            return UA_ERR_HIP;
+    } else if (split) {
         // rows of tokens past cu_seqlens_q[S] have no partials: the combine
         // leaves them alone, as the unsplit kernel does
         if (ua::launch_combine(a.o_part, a.lse_part, pl.splits,
@@ -482,7 +533,7 @@ ua_status ua_unified_attention_noalloc(const ua_attn_params *p, void *stream) {
         if (ua::noalloc_scratch(&ptr) != hipSuccess)
             return UA_ERR_HIP;
         q.workspace = ptr;
-        q.num_splits = info.num_splits;
+        q.num_splits = (info.kernels & 4) ? -info.num_splits : info.num_splits;
     } else {
         q.workspace = nullptr;
         q.workspace_bytes = 0;

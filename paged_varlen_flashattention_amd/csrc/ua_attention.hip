@@ -1332,7 +1332,7 @@ __device__ __forceinline__ void prefill_body_f8(const AttnArgs &a, int bx, uint8
 // unit u + NW are in flight while unit u is computed; no barrier until the
 // final merge of the waves' softmax states.
 template <bool F16, bool FP8KV, bool CAUSAL, bool SPLIT, int NW, bool EXT>
-__device__ __forceinline__ void decode_body(const AttnArgs &a, int bx, uint8_t *lds) {
+__device__ __forceinline__ void decode_body(const AttnArgs &a, int bx, int split, uint8_t *lds) {
     constexpr int NKB = 1;                      // 32-key blocks per unit
     constexpr int UK = 32 * NKB;                // keys per unit
     constexpr int KVB = FP8KV ? 1 : 2;
@@ -1349,7 +1349,6 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, int bx, uint8_t *
 
     const int s = bx / a.num_kv_heads;
     const int kvh = bx - s * a.num_kv_heads;
-    const int split = blockIdx.y;
     const int cu0 = a.cu_seqlens_q[s];
     const int q_len = a.cu_seqlens_q[s + 1] - cu0;
     const int G = a.group;
@@ -1545,14 +1544,51 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, int bx, uint8_t *
 // path carries none of its per-element work).
 // F8MM (fp8 caches only, without EXT): the prefill rows use the fp8-MFMA
 // body; decode rows keep the 16-bit path.
-template <bool F16, bool FP8KV, bool CAUSAL, bool SPLIT, int KG, bool EXT, bool F8MM = false>
+//
+// MIX (unsplit prefill, split decode rows: a batch that mixes both kinds of
+// sequence): the decode rows' key ranges are split num_splits ways into
+// partials that a decode-row combine merges, while prefill workgroups write
+// their rows directly.  The grid is one-dimensional in blocks of 8 positions
+// (a position's XCD is its index mod 8, so every item keeps the XCD of its
+// index and the query blocks of one kv head keep sharing an L2); the
+// mix_dblocks decode blocks are spread evenly over the first mix_region
+// blocks, so that the short split decode workgroups stream alongside the
+// prefill ones instead of taking every slot at the start.
+template <bool F16, bool FP8KV, bool CAUSAL, bool SPLIT, int KG, bool EXT, bool F8MM = false,
+          bool MIX = false>
 __global__ __launch_bounds__(kWaves * KG * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(const AttnArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[lds_bytes(kWaves * KG)];
-    const int bx = blockIdx.x;
     static_assert(!F8MM || (FP8KV && !EXT), "fp8 compute needs an fp8 cache, no mask variants");
+    static_assert(!MIX || (!SPLIT && KG == 1), "mixed launches split only the decode rows");
+    if constexpr (MIX) {
+        const int b = blockIdx.x >> 3, r = blockIdx.x & 7;
+        int c0 = a.mix_dblocks;                 // decode blocks placed before block b
+        bool dec = false;
+        if (b < a.mix_region) {
+            c0 = (int)(((int64_t)b * a.mix_dblocks) / a.mix_region);
+            dec = (int)(((int64_t)(b + 1) * a.mix_dblocks) / a.mix_region) > c0;
+        }
+        if (dec) {
+            const int d = 8 * c0 + r;           // (sequence x kv head) x split
+            if (d >= a.decode_wgs)
+                return;
+            const int pair = d / a.num_splits;
+            decode_body<F16, FP8KV, CAUSAL, true, kWaves, EXT>(a, pair, d - pair * a.num_splits, lds);
+        } else {
+            const int pi = 8 * (b - c0) + r;
+            if (pi >= a.prefill_wgs)
+                return;
+            if constexpr (F8MM)
+                prefill_body_f8<F16, CAUSAL, false, 1>(a, pi, lds);
+            else
+                prefill_body<F16, FP8KV, CAUSAL, false, 1, EXT>(a, pi, lds);
+        }
+        return;
+    }
+    const int bx = blockIdx.x;
     if (bx < a.decode_wgs)
-        decode_body<F16, FP8KV, CAUSAL, SPLIT, kWaves * KG, EXT>(a, bx, lds);
+        decode_body<F16, FP8KV, CAUSAL, SPLIT, kWaves * KG, EXT>(a, bx, blockIdx.y, lds);
     else if constexpr (F8MM)
         prefill_body_f8<F16, CAUSAL, SPLIT, KG>(a, bx - a.decode_wgs, lds);
     else
@@ -1570,17 +1606,13 @@ void attn_fwd_kernel(const AttnArgs a) {
 // stores NaN), so such a row's output is NaN rather than a plausible value.
 __device__ __forceinline__ float nan_max(float m, float x) { return (x > m || x != x) ? x : m; }
 
+// Merge the P partials of partial row `row` (of `rows` per split) into
+// output (tok, head).  One wave per row: every early return is wave-uniform.
 template <bool F16>
-__global__ __launch_bounds__(256) void combine_kernel(const float *o_part, const float *lse_part,
-                                                      int32_t P, int64_t rows, int32_t Hq, void *out,
-                                                      int64_t o_st_tok, int64_t o_st_head,
-                                                      float *lse_out, const int32_t *tok_end) {
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= rows)
-        return;
-    const int64_t tok = row / Hq;
-    if (tok_end != nullptr && tok >= (int64_t)*tok_end)
-        return;
+__device__ __forceinline__ void combine_row(const float *o_part, const float *lse_part, int32_t P,
+                                            int64_t rows, int64_t row, int64_t tok, int64_t head,
+                                            void *out, int64_t o_st_tok, int64_t o_st_head,
+                                            float *lse_out) {
     const int lane = threadIdx.x & 63;
     const int sg = lane >> 4;
     const int c = lane & 15;
@@ -1615,7 +1647,6 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *o_part, const
         return;
     // wsum > 0 is false for NaN as well: a NaN row keeps its NaN sums
     const float inv = wsum > 0.0f ? 1.0f / wsum : (wsum == 0.0f ? 0.0f : wsum);
-    const int64_t head = row - tok * Hq;
     uint8_t *op = (uint8_t *)out + (tok * o_st_tok + head * o_st_head + 8 * c) * 2;
     *(u32x4 *)op = u32x4{pack2<F16>(a0[0] * inv, a0[1] * inv), pack2<F16>(a0[2] * inv, a0[3] * inv),
                          pack2<F16>(a1[0] * inv, a1[1] * inv), pack2<F16>(a1[2] * inv, a1[3] * inv)};
@@ -1623,21 +1654,68 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *o_part, const
         lse_out[row] = wsum > 0.0f ? L + __logf(wsum) : (wsum == 0.0f ? neg_inf() : wsum);
 }
 
+template <bool F16>
+__global__ __launch_bounds__(256) void combine_kernel(const float *o_part, const float *lse_part,
+                                                      int32_t P, int64_t rows, int32_t Hq, void *out,
+                                                      int64_t o_st_tok, int64_t o_st_head,
+                                                      float *lse_out, const int32_t *tok_end) {
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows)
+        return;
+    const int64_t tok = row / Hq;
+    if (tok_end != nullptr && tok >= (int64_t)*tok_end)
+        return;
+    combine_row<F16>(o_part, lse_part, P, rows, row, tok, row - tok * Hq, out, o_st_tok, o_st_head,
+                     lse_out);
+}
+
+// The combine of a launch that split only the decode rows: one wave per
+// decode row slot (sequence, kv head, row lr < 32 of the decode body's
+// (token, head-in-group) numbering); slots of prefill, empty or short
+// sequences' missing rows are skipped, their rows written by the prefill
+// workgroups or by nobody.
+template <bool F16>
+__global__ __launch_bounds__(256) void combine_decode_kernel(
+    const float *o_part, const float *lse_part, int32_t P, int64_t rows, int32_t Hq, int32_t Hkv,
+    int32_t S, const int32_t *cu_seqlens_q, void *out, int64_t o_st_tok, int64_t o_st_head,
+    float *lse_out) {
+    const int64_t slot = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (slot >= (int64_t)S * Hkv * kDecodeRows)
+        return;
+    const int lr = (int)(slot % kDecodeRows);
+    const int pair = (int)(slot / kDecodeRows);
+    const int s = pair / Hkv;
+    const int kvh = pair - s * Hkv;
+    const int G = Hq / Hkv;
+    const int cu0 = cu_seqlens_q[s];
+    const int q_len = cu_seqlens_q[s + 1] - cu0;
+    if (q_len == 0 || q_len * G > kDecodeRows || lr >= q_len * G)
+        return;
+    const int tq = lr / G;
+    const int64_t tok = (int64_t)cu0 + tq;
+    const int64_t head = (int64_t)kvh * G + (lr - tq * G);
+    combine_row<F16>(o_part, lse_part, P, rows, tok * Hq + head, tok, head, out, o_st_tok, o_st_head,
+                     lse_out);
+}
+
 // ------------------------------------------------------------------ launchers
 
 // Launch status: the error state is cleared first, so that an error left by
 // an earlier call of the caller's is not reported as this launch's.
-template <bool F16, bool FP8KV, bool CAUSAL, bool SPLIT, int KG, bool EXT, bool F8MM = false>
+template <bool F16, bool FP8KV, bool CAUSAL, bool SPLIT, int KG, bool EXT, bool F8MM = false,
+          bool MIX = false>
 hipError_t launch_kernel(const AttnArgs &a, dim3 grid, hipStream_t st) {
     (void)hipGetLastError();
-    hipLaunchKernelGGL((attn_fwd_kernel<F16, FP8KV, CAUSAL, SPLIT, KG, EXT, F8MM>), grid,
+    hipLaunchKernelGGL((attn_fwd_kernel<F16, FP8KV, CAUSAL, SPLIT, KG, EXT, F8MM, MIX>), grid,
                        dim3(kWaves * KG * 64), 0, st, a);
     return hipGetLastError();
 }
 
-// Two key groups only for split launches.
+// Two key groups only for split launches; mix: split decode rows only.
 template <bool F16, bool FP8KV, bool CAUSAL, bool EXT, bool F8MM = false>
-hipError_t launch_shape(const AttnArgs &a, bool split, bool wide, dim3 grid, hipStream_t st) {
+hipError_t launch_shape(const AttnArgs &a, bool split, bool wide, bool mix, dim3 grid, hipStream_t st) {
+    if (mix)
+        return launch_kernel<F16, FP8KV, CAUSAL, false, 1, EXT, F8MM, true>(a, grid, st);
     if (!split)
         return launch_kernel<F16, FP8KV, CAUSAL, false, 1, EXT, F8MM>(a, grid, st);
     return wide ? launch_kernel<F16, FP8KV, CAUSAL, true, 2, EXT, F8MM>(a, grid, st)
@@ -1645,35 +1723,36 @@ hipError_t launch_shape(const AttnArgs &a, bool split, bool wide, dim3 grid, hip
 }
 
 template <bool F16, bool FP8KV>
-hipError_t launch_mode(const AttnArgs &a, bool causal, bool split, bool wide, bool ext, dim3 grid,
-                       hipStream_t st) {
+hipError_t launch_mode(const AttnArgs &a, bool causal, bool split, bool wide, bool mix, bool ext,
+                       dim3 grid, hipStream_t st) {
     if constexpr (FP8KV) {
         if (a.fp8_compute) {
             if (ext)
                 return hipErrorInvalidValue;
-            return causal ? launch_shape<F16, true, true, false, true>(a, split, wide, grid, st)
-                          : launch_shape<F16, true, false, false, true>(a, split, wide, grid, st);
+            return causal ? launch_shape<F16, true, true, false, true>(a, split, wide, mix, grid, st)
+                          : launch_shape<F16, true, false, false, true>(a, split, wide, mix, grid, st);
         }
     }
     if (causal)
-        return ext ? launch_shape<F16, FP8KV, true, true>(a, split, wide, grid, st)
-                   : launch_shape<F16, FP8KV, true, false>(a, split, wide, grid, st);
-    return ext ? launch_shape<F16, FP8KV, false, true>(a, split, wide, grid, st)
-               : launch_shape<F16, FP8KV, false, false>(a, split, wide, grid, st);
+        return ext ? launch_shape<F16, FP8KV, true, true>(a, split, wide, mix, grid, st)
+                   : launch_shape<F16, FP8KV, true, false>(a, split, wide, mix, grid, st);
+    return ext ? launch_shape<F16, FP8KV, false, true>(a, split, wide, mix, grid, st)
+               : launch_shape<F16, FP8KV, false, false>(a, split, wide, mix, grid, st);
 }
 
 }  // namespace
 
 hipError_t launch_attention(const AttnArgs &a, bool q_f16, bool kv_fp8, bool causal, bool split,
-                            bool wide, dim3 grid, hipStream_t stream) {
-    if (wide && !split)
+                            bool wide, bool mix, dim3 grid, hipStream_t stream) {
+    if ((wide && !split) || (mix && (split || a.num_splits < 2 || a.mix_region < a.mix_dblocks ||
+                                      grid.y != 1 || (int64_t)grid.x < 8LL * a.mix_dblocks)))
         return hipErrorInvalidValue;
     const bool ext = a.win_left >= 0 || a.win_right >= 0 || a.alibi != nullptr;
     if (q_f16)
-        return kv_fp8 ? launch_mode<true, true>(a, causal, split, wide, ext, grid, stream)
-                      : launch_mode<true, false>(a, causal, split, wide, ext, grid, stream);
-    return kv_fp8 ? launch_mode<false, true>(a, causal, split, wide, ext, grid, stream)
-                  : launch_mode<false, false>(a, causal, split, wide, ext, grid, stream);
+        return kv_fp8 ? launch_mode<true, true>(a, causal, split, wide, mix, ext, grid, stream)
+                      : launch_mode<true, false>(a, causal, split, wide, mix, ext, grid, stream);
+    return kv_fp8 ? launch_mode<false, true>(a, causal, split, wide, mix, ext, grid, stream)
+                  : launch_mode<false, false>(a, causal, split, wide, mix, ext, grid, stream);
 }
 
 // ------------------------------------------------------------------ no-allocation scratch
@@ -1722,6 +1801,25 @@ hipError_t launch_combine(const float *o_part, const float *lse_part, int32_t nu
     else
         hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(256), 0, stream, o_part, lse_part,
                            num_splits, rows, num_q_heads, out, o_st_tok, o_st_head, lse_out, tok_end);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine_decode(const float *o_part, const float *lse_part, int32_t num_splits,
+                                 int64_t rows, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t num_seqs, const int32_t *cu_seqlens_q, void *out,
+                                 bool out_f16, int64_t o_st_tok, int64_t o_st_head, float *lse_out,
+                                 hipStream_t stream) {
+    const int64_t slots = (int64_t)num_seqs * num_kv_heads * kDecodeRows;
+    const dim3 grid((unsigned)((slots + 3) / 4));
+    (void)hipGetLastError();
+    if (out_f16)
+        hipLaunchKernelGGL(combine_decode_kernel<true>, grid, dim3(256), 0, stream, o_part, lse_part,
+                           num_splits, rows, num_q_heads, num_kv_heads, num_seqs, cu_seqlens_q, out,
+                           o_st_tok, o_st_head, lse_out);
+    else
+        hipLaunchKernelGGL(combine_decode_kernel<false>, grid, dim3(256), 0, stream, o_part, lse_part,
+                           num_splits, rows, num_q_heads, num_kv_heads, num_seqs, cu_seqlens_q, out,
+                           o_st_tok, o_st_head, lse_out);
     return hipGetLastError();
 }
 

@@ -44,6 +44,10 @@ struct AttnArgs {
     const float *alibi;            // [Hq] ALiBi slopes, or null
     int32_t fp8_compute;           // fp8 caches: prefill rows use fp8 MFMA (Q, P rounded to e4m3)
     int32_t spin_limit;            // polls per key-group barrier before it gives up (outputs NaN)
+    // mixed launches (prefill rows unsplit, decode rows split num_splits ways):
+    int32_t prefill_wgs;           // prefill workgroups (query block slots x kv heads)
+    int32_t mix_dblocks;           // blocks of 8 decode workgroups, ceil(decode_wgs / 8)
+    int32_t mix_region;            // the decode blocks are spread over grid blocks [0, mix_region)
 };
 
 constexpr int kPrefillBlockM = 128;   // query rows per prefill workgroup
@@ -55,9 +59,12 @@ constexpr int kWaves = 4;             // wavefronts per workgroup, both bodies
 // by prefill workgroups (slots x Hkv), grid.y = splits.  q_f16: q/out are fp16 (else
 // bf16); kv_fp8: the cache holds fp8 e4m3fn codes (else the q dtype); wide
 // (split launches only): 8-wave workgroups, each prefill workgroup running two
-// key groups over alternate tiles of its split.
+// key groups over alternate tiles of its split.  mix (split = false): only the
+// decode rows are split, num_splits ways; decode_wgs = S x Hkv x num_splits,
+// prefill_wgs = slots x Hkv, and the one-dimensional grid holds
+// 8 x (mix_dblocks + ceil(prefill_wgs / 8)) workgroups.
 hipError_t launch_attention(const AttnArgs &a, bool q_f16, bool kv_fp8, bool causal, bool split,
-                            bool wide, dim3 grid, hipStream_t stream);
+                            bool wide, bool mix, dim3 grid, hipStream_t stream);
 
 // Enqueue the split combine kernel over rows = T * Hq rows.  tok_end:
 // optional device pointer to the token count that sequences cover
@@ -66,6 +73,15 @@ hipError_t launch_combine(const float *o_part, const float *lse_part, int32_t nu
                           int64_t rows, int32_t num_q_heads, void *out, bool out_f16,
                           int64_t o_st_tok, int64_t o_st_head, float *lse_out,
                           const int32_t *tok_end, hipStream_t stream);
+
+// Enqueue the combine of a mixed launch: only the rows of decode sequences
+// (q_len * Hq / Hkv <= kDecodeRows) are merged; rows = T * Hq rows per split
+// in the partial arrays.
+hipError_t launch_combine_decode(const float *o_part, const float *lse_part, int32_t num_splits,
+                                 int64_t rows, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t num_seqs, const int32_t *cu_seqlens_q, void *out,
+                                 bool out_f16, int64_t o_st_tok, int64_t o_st_head, float *lse_out,
+                                 hipStream_t stream);
 
 // Device address of this GPU's no-allocation scratch array
 // (UA_NOALLOC_SCRATCH_BYTES bytes, 256-byte aligned), looked up once per device.

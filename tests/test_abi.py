@@ -137,7 +137,7 @@ def test_plan_split_prefill_is_wide(lib):
     ("num_seqs", -1, B.UA_ERR_INVALID_ARG),
     ("num_tokens", -5, B.UA_ERR_INVALID_ARG),
     ("num_splits", 129, B.UA_ERR_INVALID_ARG),
-    ("num_splits", -1, B.UA_ERR_INVALID_ARG),
+    ("num_splits", -129, B.UA_ERR_INVALID_ARG),
     ("q_dtype", B.UA_FP8_E4M3FN, B.UA_ERR_UNSUPPORTED),
     ("q_dtype", 9, B.UA_ERR_INVALID_ARG),
     ("kv_dtype", B.UA_FP16, B.UA_ERR_UNSUPPORTED),
@@ -234,6 +234,72 @@ def test_split_needs_workspace(lib):
     st, info = plan_status(lib, p)
     assert st == 0 and info.num_splits == 8 and info.grid_y == 8
     assert lib.ua_unified_attention(ctypes.byref(base_params(num_splits=8)), None) == B.UA_ERR_WORKSPACE
+
+
+MIXED = dict(num_seqs=68, num_tokens=8256, num_q_heads=64, num_kv_heads=8, max_seqlen_q=2048,
+             max_seqlen_k=16384, block_table_stride=1024, q_stride_token=64 * 128,
+             o_stride_token=64 * 128)
+
+
+def test_plan_mixed_splits_decode_rows_only(lib):
+    # 64 decode sequences + 4 prefill chunks of 2048 tokens (G = 8): automatic
+    # choice keeps the prefill rows unsplit and splits the decode rows, one
+    # split per 4096 keys of max_seqlen_k (16384 -> 4), in 4-wave workgroups
+    # on a one-dimensional grid
+    need = lib.ua_workspace_size(8256, 64, 128, 4)
+    st, info = plan_status(lib, base_params(num_splits=0, workspace=FAKE, workspace_bytes=need,
+                                            **MIXED))
+    assert st == 0 and info.kernels == 7 and info.num_splits == 4 and info.num_waves == 4
+    assert info.grid_y == 1 and info.decode_grid_x == 68 * 8 * 4
+    p = base_params(num_splits=0, workspace=FAKE, workspace_bytes=1 << 40, **MIXED)
+    p.max_seqlen_k, p.block_table_stride = 65536, 4096
+    st, info = plan_status(lib, p)
+    assert st == 0 and info.kernels == 7 and info.num_splits == 8          # at most 8
+    assert info.grid_x == (8256 // 16 + 68) * 8
+    # a workspace for 3 splits only: 3 decode splits; none: unsplit
+    st, info = plan_status(lib, base_params(num_splits=0, workspace=FAKE,
+                                            workspace_bytes=lib.ua_workspace_size(8256, 64, 128, 3),
+                                            **MIXED))
+    assert st == 0 and info.kernels == 7 and info.num_splits == 3
+    st, info = plan_status(lib, base_params(num_splits=0, **MIXED))
+    assert st == 0 and info.kernels == 3 and info.num_splits == 1 and info.decode_grid_x == 68 * 8
+    # explicit -4: decode rows split 4 ways; -1: unsplit; 4: every row split
+    st, info = plan_status(lib, base_params(num_splits=-4, workspace=FAKE,
+                                            workspace_bytes=lib.ua_workspace_size(8256, 64, 128, 4),
+                                            **MIXED))
+    assert st == 0 and info.kernels == 7 and info.num_splits == 4 and info.grid_y == 1
+    assert plan_status(lib, base_params(num_splits=-4, **MIXED))[0] == B.UA_ERR_WORKSPACE
+    st, info = plan_status(lib, base_params(num_splits=-1, **MIXED))
+    assert st == 0 and info.kernels == 3 and info.num_splits == 1
+    st, info = plan_status(lib, base_params(num_splits=4, workspace=FAKE,
+                                            workspace_bytes=lib.ua_workspace_size(8256, 64, 128, 4),
+                                            **MIXED))
+    assert st == 0 and info.kernels == 3 and info.grid_y == 4 and info.num_waves == 8
+
+
+def test_plan_no_decode_split_without_decode_rows(lib):
+    # dense 4 x 4096 (G = 1): every sequence has 4096 tokens, none can be a
+    # decode sequence, so automatic choice leaves the launch unsplit
+    p = base_params(num_splits=0, num_seqs=4, num_tokens=16384, num_q_heads=32, num_kv_heads=32,
+                    max_seqlen_q=4096, max_seqlen_k=4096, block_table_stride=256,
+                    q_stride_token=32 * 128, o_stride_token=32 * 128,
+                    kv_stride_block=16 * 32 * 128, kv_stride_slot=32 * 128,
+                    workspace=FAKE, workspace_bytes=1 << 40)
+    st, info = plan_status(lib, p)
+    assert st == 0 and info.kernels == 3 and info.num_splits == 1
+    # the bound T - (S - 1) * max_q <= 32 / G: 33 tokens left for the
+    # shortest sequence rule a decode sequence out, 32 do not
+    p.num_tokens = 3 * 4096 + 33
+    st, info = plan_status(lib, p)
+    assert st == 0 and info.kernels == 3 and info.num_splits == 1
+    p.num_tokens = 3 * 4096 + 32
+    p.max_seqlen_k, p.block_table_stride = 8192, 512
+    st, info = plan_status(lib, p)
+    assert st == 0 and info.kernels == 7 and info.num_splits == 2
+    # decode-only launches: -n is an ordinary split
+    st, info = plan_status(lib, base_params(num_splits=-4, workspace=FAKE,
+                                            workspace_bytes=lib.ua_workspace_size(256, 32, 128, 4)))
+    assert st == 0 and info.kernels == 2 and info.num_splits == 4 and info.grid_y == 4
 
 
 def test_auto_splits_respect_workspace(lib):

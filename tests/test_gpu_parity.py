@@ -96,6 +96,98 @@ def test_config2_full_size_whole_planes(causal):
     H.compare(wl, out, lse, rows=rows, what="config2 whole planes")
 
 
+
+# ------------------------------------------------------------------ mixed launches: decode rows split
+
+def decode_token_mask(wl):
+    """Tokens of decode sequences (q_len * G <= 32 query rows): the rows that a
+    mixed launch splits."""
+    G = wl.num_q_heads // wl.num_kv_heads
+    cu = wl.cu_seqlens_q.numpy()
+    m = np.zeros(wl.num_tokens, dtype=bool)
+    for s in range(wl.num_seqs):
+        ql = int(cu[s + 1] - cu[s])
+        if 0 < ql and ql * G <= 32:
+            m[cu[s]:cu[s + 1]] = True
+    return m
+
+
+def check_mixed(wl, splits, d=None, fp8_compute=False, what=""):
+    """A mixed launch (decode rows split, prefill rows unsplit) against the
+    unsplit launch and the oracle: prefill rows bit for bit equal to the
+    unsplit launch (the same unsplit prefill path), every row within the
+    oracle's bar (decode rows through their partials and the decode-row
+    combine)."""
+    info = H.plan(wl, splits)
+    assert info.kernels & 4 and info.num_splits == abs(splits), info.as_dict()
+    d = d or H.to_device(wl)
+    out, lse = H.run(wl, d, num_splits=splits, fp8_compute=fp8_compute)
+    out1, lse1 = H.run(wl, d, num_splits=1, fp8_compute=fp8_compute)
+    dec = torch.from_numpy(decode_token_mask(wl)).cuda()
+    assert dec.any() and (~dec).any(), "a mixed case needs both kinds of sequence"
+    pre = ~dec
+    assert torch.equal(out[pre].view(torch.int16), out1[pre].view(torch.int16)), f"{what}: prefill rows"
+    assert torch.equal(lse[pre], lse1[pre]), f"{what}: prefill lse"
+    if fp8_compute:
+        rows = np.array([(t, h) for t in np.nonzero(decode_token_mask(wl))[0]
+                         for h in range(wl.num_q_heads)])
+        return H.compare(wl, out, lse, rows=rows, what=what + " decode rows")
+    return H.compare(wl, out, lse, what=what)
+
+
+# (q_lens, kv_lens, (Hq, Hkv), block size, q dtype, kv dtype, causal, splits)
+MIX_CASES = [
+    ([1, 150, 1, 4, 1], [2500, 1500, 64, 1200, 4097], (64, 8), 32, "bf16", None, True, -5),
+    ([1, 150, 1, 4, 1], [2500, 1500, 64, 1200, 4097], (64, 8), 32, "fp16", None, False, -2),
+    ([32, 1, 33, 0, 1], [600, 3000, 800, 50, 1], (8, 8), 16, "bf16", None, True, -16),
+    ([10, 11, 1, 0, 2], [900, 400, 2049, 7, 2], (6, 2), 64, "fp16", None, True, -4),
+    ([1, 300, 2, 1], [5000, 700, 3000, 130], (32, 8), 16, "bf16", "fp8_e4m3fn", True, -8),
+    ([1, 1, 40, 1, 1, 1], [4096, 8192, 500, 17, 2048, 6000], (16, 2), 16, "bf16", None, True, -4),
+    ([3, 129, 1], [3, 129, 1], (8, 1), 128, "bf16", None, True, -3),
+]
+
+
+@pytest.mark.parametrize("case", range(len(MIX_CASES)))
+def test_mixed_decode_split(case):
+    q_lens, kv_lens, heads, bs, dtype, kv_dtype, causal, splits = MIX_CASES[case]
+    wl = wk.make_paged("mixsplit", 5200 + case, q_lens, kv_lens, heads[0], heads[1], block_size=bs,
+                       dtype=dtype, kv_dtype=kv_dtype, causal=causal)
+    H.say(f"mixed decode split case={case} q={q_lens} kv={kv_lens} heads={heads} splits={splits}")
+    check_mixed(wl, splits, what=f"mixed {case}")
+
+
+@pytest.mark.parametrize("mask", ["window", "alibi"])
+def test_mixed_decode_split_window_alibi(mask):
+    wl = wk.make_paged("mixmask", 5300, [1, 90, 1, 2], [3000, 900, 70, 2200], 32, 8, block_size=16,
+                       causal=True)
+    wl = (wk.with_mask(wl, 300, -1, name="mix_window") if mask == "window"
+          else wk.with_mask(wl, alibi=wk.alibi_slopes(32), name="mix_alibi"))
+    H.say(f"mixed decode split with {mask}")
+    check_mixed(wl, -3, what=f"mixed {mask}")
+
+
+def test_mixed_decode_split_fp8_compute():
+    wl = wk.make_paged("mixf8", 5400, [1, 200, 1, 3], [4000, 1000, 33, 2500], 64, 8, block_size=16,
+                       kv_dtype="fp8_e4m3fn", causal=True)
+    H.say("mixed decode split, fp8 compute prefill rows")
+    check_mixed(wl, -6, fp8_compute=True, what="mixed fp8 compute")
+
+
+def test_config4_mixed_decode_split_auto():
+    # the mixed chunked-prefill batch as the planner runs it: one decode
+    # split per 4096 keys of the longest sequence
+    wl = wk.config4()
+    H.say(f"config4 mixed chunked prefill, automatic decode split, max_seqlen_k {wl.max_seqlen_k}")
+    info = H.plan(wl, 0)
+    assert info.kernels == 7 and info.num_splits == min(8, wl.max_seqlen_k // 4096), info.as_dict()
+    d = H.to_device(wl)
+    out, lse = H.run(wl, d, num_splits=0)
+    out1, lse1 = H.run(wl, d, num_splits=1)
+    assert torch.equal(out[64:].view(torch.int16), out1[64:].view(torch.int16)), "prefill rows"
+    assert torch.equal(lse[64:], lse1[64:]), "prefill lse"
+    decode_rows = np.array([(t, h) for t in range(64) for h in range(wl.num_q_heads)])
+    H.compare(wl, out, lse, rows=decode_rows, what="config4 decode rows, split")
+
 # ------------------------------------------------------------------ sweeps and edge cases
 
 @pytest.mark.parametrize("seed", range(24))
@@ -387,20 +479,20 @@ def test_deterministic():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16)) and torch.equal(la, lb)
 
 
-@pytest.mark.parametrize("splits", [1, 4])
+@pytest.mark.parametrize("splits", [1, 4, -4])
 def test_hip_graph_capture_replays(splits):
     """The call holds no host synchronisation, copy or memset, so a caller can
     capture it (and, with splits, the combine launch) into a HIP graph: after
     the queries are overwritten in place by eager work, each replay must equal
     an eager call bit for bit, and the last one the oracle."""
-    wl = wk.make_paged("graph", 4500 + splits, [1, 1, 37, 130], [500, 70, 300, 130], 8, 2,
+    wl = wk.make_paged("graph", 4500 + abs(splits), [1, 1, 37, 130], [500, 70, 300, 130], 8, 2,
                        block_size=16, causal=True)
     H.say(f"graph capture splits={splits}")
     d = H.to_device(wl)
     T, Hq = wl.num_tokens, wl.num_q_heads
     ws = None
-    if splits > 1:
-        ws = torch.empty(B.workspace_size(T, Hq, 128, splits), dtype=torch.uint8, device="cuda")
+    if abs(splits) > 1:
+        ws = torch.empty(B.workspace_size(T, Hq, 128, abs(splits)), dtype=torch.uint8, device="cuda")
     out = torch.empty_like(d["q"])
     lse = torch.empty(T, Hq, dtype=torch.float32, device="cuda")
 
@@ -420,7 +512,7 @@ def test_hip_graph_capture_replays(splits):
     with torch.cuda.graph(graph):
         call()
     torch.cuda.synchronize()
-    gen = torch.Generator().manual_seed(4500 + splits)
+    gen = torch.Generator().manual_seed(4500 + abs(splits))
     for rep in range(3):
         q_new = torch.randn(tuple(wl.q.shape), generator=gen).to(wl.q.dtype)
         d["q"].copy_(q_new)
@@ -521,14 +613,14 @@ def test_key_group_barrier_timeout_is_visible(fp8):
     H.compare(wl, out2, lse2, what="the next call without the hook")
 
 
-@pytest.mark.parametrize("splits", [1, 3])
+@pytest.mark.parametrize("splits", [1, 3, -3])
 def test_padding_rows_and_workspace_guards(splits):
     """Tokens past cu_seqlens_q[S] (padding) belong to no sequence: their out
     and lse rows stay untouched with and without splits; the split workspace
     sits between guard regions that must stay untouched, and out inside a
     larger buffer whose guard rows must too."""
-    wl = wk.make_paged("pad", 4900 + splits, [1, 70, 1, 9], [500, 300, 77, 9], 8, 2, block_size=16,
-                       causal=True)
+    wl = wk.make_paged("pad", 4900 + abs(splits), [1, 70, 1, 9], [500, 300, 77, 9], 8, 2,
+                       block_size=16, causal=True)
     T, Hq, D = wl.q.shape
     pad = 6
     d = H.to_device(wl)
@@ -541,8 +633,8 @@ def test_padding_rows_and_workspace_guards(splits):
     lse = lse_big[1:T + pad + 1]
     lse[:T].fill_(float("nan"))
     ws = guard = None
-    if splits > 1:
-        n = B.workspace_size(T + pad, Hq, D, splits)
+    if abs(splits) > 1:
+        n = B.workspace_size(T + pad, Hq, D, abs(splits))
         g = 4096
         guard = torch.full((n + 2 * g,), 0xA5, dtype=torch.uint8, device="cuda")
         ws = guard[g:g + n]

@@ -29,7 +29,8 @@ def both(wl, splits):
         if noalloc:
             ua.unified_attention_noalloc(*args, num_splits=splits, lse=lse)
         else:
-            ws = torch.empty(max(1, B.workspace_size(T, Hq, 128, splits)), dtype=torch.uint8, device="cuda")
+            ws = torch.empty(max(1, B.workspace_size(T, Hq, 128, abs(splits))), dtype=torch.uint8,
+                             device="cuda")
             ua.unified_attention(*args, num_splits=splits, lse=lse, workspace=ws)
         torch.cuda.synchronize()
         outs.append((out, lse))
@@ -65,3 +66,21 @@ def test_noalloc_unsplit_and_auto():
                                      wl.softmax_scale, wl.causal, num_splits=splits, lse=lse)
         torch.cuda.synchronize()
         H.compare(wl, out, lse, what=f"noalloc splits {splits}")
+
+
+def test_noalloc_decode_rows_split():
+    # a mixed batch whose decode rows alone are split (-4), then a smaller one
+    # (-2): the scratch keeps only the decode rows' partials
+    cases = [
+        (wk.make_paged("noalloc_d", 5003, [1, 90, 1, 4], [3000, 700, 64, 2100], 64, 8, block_size=16,
+                       causal=True), -4),
+        (wk.make_paged("noalloc_e", 5004, [2, 50], [900, 60], 32, 8, block_size=32, causal=False), -2),
+    ]
+    for wl, splits in cases:
+        info = H.plan(wl, splits)
+        assert info.kernels & 4 and info.num_splits == -splits, info.as_dict()
+        H.say(f"noalloc {wl.name} T={wl.num_tokens} decode-row splits={-splits}")
+        (o_ws, l_ws), (o_na, l_na) = both(wl, splits)
+        assert torch.equal(o_ws.view(torch.int16), o_na.view(torch.int16)), "outputs differ"
+        assert torch.equal(l_ws, l_na), "lse differs"
+        H.compare(wl, o_na, l_na, what=f"noalloc {wl.name}")
