@@ -203,7 +203,10 @@ typedef struct ua_attn_params {
  * runs; otherwise both run and the prefill kernel skips the short sequences.
  * Split launches with prefill work use 8-wave workgroups: two groups of 4
  * prefill waves take alternate tiles of the split and merge, and the decode
- * body streams with 8 waves.  A launch that splits only the decode rows
+ * body streams with 8 waves; when such a launch has at most 8 x 256
+ * workgroups' worth of items ((grid_x + decode_grid_x) x grid_y), it runs as
+ * min(items, 256) workgroups, workgroup w taking items w, w + 256, ... in
+ * grid order.  A launch that splits only the decode rows
  * (kernels bit 2) keeps 4-wave workgroups: decode_grid_x decode workgroups
  * (sequence x kv head x split) spread among the grid_x prefill workgroups in
  * one dimension, grid_y = 1. */

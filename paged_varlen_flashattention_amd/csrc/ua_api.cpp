@@ -29,6 +29,9 @@ constexpr int kBarrierPolls = 1 << 20;   // polls before a key-group barrier wai
 // of the longest sequence, at most kMaxDecodeSplits.
 constexpr int kDecodeSplitKeys = 4096;
 constexpr int kMaxDecodeSplits = 8;
+// Split launches with prefill work (whole-CU workgroups) of at most this many
+// items per CU run as one persistent workgroup per CU.
+constexpr int kPersistItemsPerCU = 8;
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 bool pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
@@ -474,12 +477,21 @@ ua_status ua_unified_attention(const ua_attn_params *p, void *stream) {
 
     a.decode_wgs = (int32_t)info.decode_grid_x;
     dim3 grid((unsigned)(info.grid_x + info.decode_grid_x), (unsigned)info.grid_y);
+    if (pl.wide && (info.grid_x + info.decode_grid_x) * info.grid_y <= kPersistItemsPerCU * kNumCUs) {
+        // whole-CU workgroups, few items: one persistent workgroup per CU
+        // walks the items in grid order (see the kernel's persistent loop)
+        const int64_t items = (info.grid_x + info.decode_grid_x) * info.grid_y;
+        a.persist_items = (int32_t)items;
+        a.row_items = (int32_t)(info.grid_x + info.decode_grid_x);
+        grid = dim3((unsigned)std::min<int64_t>(items, kNumCUs), 1);
+    }
     if (pl.mix) {
-        // decode blocks spread over the whole grid (see the kernel's MIX entry)
+        // decode blocks spread over the first half of the grid (see the
+        // kernel's MIX entry)
         const int64_t nd = (info.decode_grid_x + 7) / 8, np = (info.grid_x + 7) / 8;
         a.prefill_wgs = (int32_t)info.grid_x;
         a.mix_dblocks = (int32_t)nd;
-        a.mix_region = (int32_t)(nd + np);
+        a.mix_region = (int32_t)(nd + np / 2);
         grid = dim3((unsigned)(8 * (nd + np)), 1);
     }
     a.win_left = p->window_left;

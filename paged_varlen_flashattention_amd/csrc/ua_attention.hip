@@ -570,12 +570,13 @@ struct PrefillBlock {
 };
 
 template <bool CAUSAL, bool SPLIT, bool EXT>
-__device__ __forceinline__ bool locate_block(const AttnArgs &a, int bx, int TN, PrefillBlock &B) {
+__device__ __forceinline__ bool locate_block(const AttnArgs &a, int bx, int split, int TN,
+                                             PrefillBlock &B) {
     B.kvh = bx % a.num_kv_heads;
     int slot = bx / a.num_kv_heads;
     if (CAUSAL)
         slot = a.num_qslots - 1 - slot;         // late (long) query blocks first
-    B.split = blockIdx.y;
+    B.split = split;
     int lo = 0, hi = a.num_seqs - 1;
     while (lo < hi) {                           // largest s with cu[s]/BLOCK_Q + s <= slot
         const int mid = (lo + hi + 1) >> 1;
@@ -630,7 +631,7 @@ __device__ __forceinline__ bool locate_block(const AttnArgs &a, int bx, int TN, 
 // softmax states are merged at the end (KG = 2 gives two waves per SIMD where
 // a launch has only about one workgroup per CU).
 template <bool F16, bool FP8KV, bool CAUSAL, bool SPLIT, int KG, bool EXT>
-__device__ __forceinline__ void prefill_body(const AttnArgs &a, int bx, uint8_t *lds) {
+__device__ __forceinline__ void prefill_body(const AttnArgs &a, int bx, int split_ix, uint8_t *lds) {
     constexpr int NT = 256, TN = 64;
     constexpr int NKB = TN / 32;                // 32-key blocks per tile
     constexpr int KVB = FP8KV ? 1 : 2;          // bytes per cached element
@@ -666,7 +667,7 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, int bx, uint8_t 
 
     // ---------------------------------------------------------------- tiler
     PrefillBlock B;
-    if (!locate_block<CAUSAL, SPLIT, EXT>(a, bx, TN, B))
+    if (!locate_block<CAUSAL, SPLIT, EXT>(a, bx, split_ix, TN, B))
         return;                                 // uniform, before any barrier
     const int kvh = B.kvh, split = B.split, s = B.s, cu0 = B.cu0;
     const int tq0 = B.tq0, tq1 = B.tq1, kv_len = B.kv_len, ctx = B.ctx, kv_end = B.kv_end;
@@ -995,7 +996,7 @@ __device__ __forceinline__ int gv_swz(int k) { return (k >> 1) & 3; }
 __device__ __forceinline__ int pk_row(int i) { return 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3); }
 
 template <bool F16, bool CAUSAL, bool SPLIT, int KG>
-__device__ __forceinline__ void prefill_body_f8(const AttnArgs &a, int bx, uint8_t *lds) {
+__device__ __forceinline__ void prefill_body_f8(const AttnArgs &a, int bx, int split_ix, uint8_t *lds) {
     constexpr int NT = 256, TN = 64;
     constexpr int TB = TN * 128;                // bytes of one K (or V) tile of codes
     constexpr int STAGE = 2 * TB;
@@ -1026,7 +1027,7 @@ __device__ __forceinline__ void prefill_body_f8(const AttnArgs &a, int bx, uint8
     };
 
     PrefillBlock B;
-    if (!locate_block<CAUSAL, SPLIT, false>(a, bx, TN, B))
+    if (!locate_block<CAUSAL, SPLIT, false>(a, bx, split_ix, TN, B))
         return;
     const int kvh = B.kvh, split = B.split, s = B.s, cu0 = B.cu0;
     const int tq0 = B.tq0, tq1 = B.tq1, kv_len = B.kv_len, ctx = B.ctx, kv_end = B.kv_end;
@@ -1432,8 +1433,10 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, int bx, int split
             const int jb = u * UK + VKI * i;
             const int64_t pofs = ((int64_t)(VKI * i < 16 ? ids[0] : ids[1]) * a.kv_st_blk +
                                   (int64_t)(jb & bs_mask) * a.kv_st_slot) * KVB;
-            kr[i] = *(const u32x4 *)(kbase + pofs + vlofs);
-            vr[i] = *(const u32x4 *)(vbase + pofs + vlofs);
+            // streamed once: non-temporal, so the stream does not evict
+            // what other workgroups reuse from the L2
+            kr[i] = __builtin_nontemporal_load((const u32x4 *)(kbase + pofs + vlofs));
+            vr[i] = __builtin_nontemporal_load((const u32x4 *)(vbase + pofs + vlofs));
         }
     };
     uint8_t *const sK = lds + wv * (2 * VST);
@@ -1552,8 +1555,9 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, int bx, int split
 // (a position's XCD is its index mod 8, so every item keeps the XCD of its
 // index and the query blocks of one kv head keep sharing an L2); the
 // mix_dblocks decode blocks are spread evenly over the first mix_region
-// blocks, so that the short split decode workgroups stream alongside the
-// prefill ones instead of taking every slot at the start.
+// blocks (the first half of the grid), so that the short split decode
+// workgroups stream alongside the prefill ones instead of taking every slot
+// at the start, and are done well before the last prefill workgroups.
 template <bool F16, bool FP8KV, bool CAUSAL, bool SPLIT, int KG, bool EXT, bool F8MM = false,
           bool MIX = false>
 __global__ __launch_bounds__(kWaves * KG * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -1580,19 +1584,37 @@ void attn_fwd_kernel(const AttnArgs a) {
             if (pi >= a.prefill_wgs)
                 return;
             if constexpr (F8MM)
-                prefill_body_f8<F16, CAUSAL, false, 1>(a, pi, lds);
+                prefill_body_f8<F16, CAUSAL, false, 1>(a, pi, 0, lds);
             else
-                prefill_body<F16, FP8KV, CAUSAL, false, 1, EXT>(a, pi, lds);
+                prefill_body<F16, FP8KV, CAUSAL, false, 1, EXT>(a, pi, 0, lds);
         }
         return;
+    }
+    if constexpr (SPLIT && KG == 2) {
+        // persistent: the workgroups take items i, i + gridDim.x, ... of the
+        // (split x (decode, prefill)) grid order, so that items which exit at
+        // once do not occupy CUs the working ones are then placed behind
+        if (a.persist_items > 0) {
+            for (int it = blockIdx.x; it < a.persist_items; it += gridDim.x) {
+                __syncthreads();                // every wave is done with the last item's LDS
+                const int y = it / a.row_items, x = it - y * a.row_items;
+                if (x < a.decode_wgs)
+                    decode_body<F16, FP8KV, CAUSAL, SPLIT, kWaves * KG, EXT>(a, x, y, lds);
+                else if constexpr (F8MM)
+                    prefill_body_f8<F16, CAUSAL, SPLIT, KG>(a, x - a.decode_wgs, y, lds);
+                else
+                    prefill_body<F16, FP8KV, CAUSAL, SPLIT, KG, EXT>(a, x - a.decode_wgs, y, lds);
+            }
+            return;
+        }
     }
     const int bx = blockIdx.x;
     if (bx < a.decode_wgs)
         decode_body<F16, FP8KV, CAUSAL, SPLIT, kWaves * KG, EXT>(a, bx, blockIdx.y, lds);
     else if constexpr (F8MM)
-        prefill_body_f8<F16, CAUSAL, SPLIT, KG>(a, bx - a.decode_wgs, lds);
+        prefill_body_f8<F16, CAUSAL, SPLIT, KG>(a, bx - a.decode_wgs, blockIdx.y, lds);
     else
-        prefill_body<F16, FP8KV, CAUSAL, SPLIT, KG, EXT>(a, bx - a.decode_wgs, lds);
+        prefill_body<F16, FP8KV, CAUSAL, SPLIT, KG, EXT>(a, bx - a.decode_wgs, blockIdx.y, lds);
 }
 
 // ------------------------------------------------------------------ combine kernel

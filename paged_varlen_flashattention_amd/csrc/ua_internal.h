@@ -48,6 +48,11 @@ struct AttnArgs {
     int32_t prefill_wgs;           // prefill workgroups (query block slots x kv heads)
     int32_t mix_dblocks;           // blocks of 8 decode workgroups, ceil(decode_wgs / 8)
     int32_t mix_region;            // the decode blocks are spread over grid blocks [0, mix_region)
+    // persistent split launches with prefill work (two key groups): items
+    // [0, persist_items) in grid order, row_items (decode + prefill
+    // workgroups) per split; 0 = one workgroup per item
+    int32_t persist_items;
+    int32_t row_items;
 };
 
 constexpr int kPrefillBlockM = 128;   // query rows per prefill workgroup
