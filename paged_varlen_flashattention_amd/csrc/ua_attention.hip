@@ -631,7 +631,8 @@ __device__ __forceinline__ bool locate_block(const AttnArgs &a, int bx, int spli
 // softmax states are merged at the end (KG = 2 gives two waves per SIMD where
 // a launch has only about one workgroup per CU).
 template <bool F16, bool FP8KV, bool CAUSAL, bool SPLIT, int KG, bool EXT>
-__device__ __forceinline__ void prefill_body(const AttnArgs &a, int bx, int split_ix, uint8_t *lds) {
+__device__ __forceinline__ void prefill_body(const AttnArgs &a, int bx, int split_ix, int tid_in,
+                                             uint8_t *lds) {
     constexpr int NT = 256, TN = 64;
     constexpr int NKB = TN / 32;                // 32-key blocks per tile
     constexpr int KVB = FP8KV ? 1 : 2;          // bytes per cached element
@@ -641,7 +642,7 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, int bx, int spli
                       (KG == 1 || 4 * kDecodeMergeRows * 64 * 4 <= KG * 2 * STAGE),
                   "stages, counters and merge records fit");
 
-    const int tid = threadIdx.x;
+    const int tid = tid_in;
     const int grp = KG == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid >> 8);   // key group
     const int gtid = tid & (NT - 1);            // thread within the group
     const int lane = tid & 63;
@@ -996,13 +997,14 @@ __device__ __forceinline__ int gv_swz(int k) { return (k >> 1) & 3; }
 __device__ __forceinline__ int pk_row(int i) { return 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3); }
 
 template <bool F16, bool CAUSAL, bool SPLIT, int KG>
-__device__ __forceinline__ void prefill_body_f8(const AttnArgs &a, int bx, int split_ix, uint8_t *lds) {
+__device__ __forceinline__ void prefill_body_f8(const AttnArgs &a, int bx, int split_ix, int tid_in,
+                                                uint8_t *lds) {
     constexpr int NT = 256, TN = 64;
     constexpr int TB = TN * 128;                // bytes of one K (or V) tile of codes
     constexpr int STAGE = 2 * TB;
     static_assert(KG == 1 || KG == 2, "one or two key groups");
 
-    const int tid = threadIdx.x;
+    const int tid = tid_in;
     const int grp = KG == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid >> 8);
     const int gtid = tid & (NT - 1);
     const int lane = tid & 63;
@@ -1333,7 +1335,8 @@ __device__ __forceinline__ void prefill_body_f8(const AttnArgs &a, int bx, int s
 // unit u + NW are in flight while unit u is computed; no barrier until the
 // final merge of the waves' softmax states.
 template <bool F16, bool FP8KV, bool CAUSAL, bool SPLIT, int NW, bool EXT>
-__device__ __forceinline__ void decode_body(const AttnArgs &a, int bx, int split, uint8_t *lds) {
+__device__ __forceinline__ void decode_body(const AttnArgs &a, int bx, int split, int tid_in,
+                                            uint8_t *lds) {
     constexpr int NKB = 1;                      // 32-key blocks per unit
     constexpr int UK = 32 * NKB;                // keys per unit
     constexpr int KVB = FP8KV ? 1 : 2;
@@ -1341,7 +1344,7 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, int bx, int split
     constexpr int MROWS = kDecodeMergeRows;
     static_assert(NW * 2 * VST <= lds_bytes(NW) && NW * MROWS * 64 * 4 <= lds_bytes(NW), "LDS budget");
 
-    const int tid = threadIdx.x;
+    const int tid = tid_in;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int hl = lane >> 5;
@@ -1426,8 +1429,14 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, int bx, int split
     const int vkey = lane / VLK;
     const int vch = lane % VLK;                 // 16-byte chunk of the cached row
     const uint32_t vlofs = (uint32_t)(vkey * a.kv_st_slot * KVB + 16 * vch);
-    u32x4 kr[VNI], vr[VNI];
-    auto load_kv = [&](int u) {
+    // units in flight per wave: two for fp8 caches (their register sets are
+    // half as large), one for 16-bit caches (a second set would spill)
+    constexpr int NSET = FP8KV ? 2 : 1;
+    u32x4 kr[NSET][VNI], vr[NSET][VNI];
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, NSET - 1>;
+    auto load_kv = [&](int u, auto set) {
+        constexpr int SI = decltype(set)::value;
 #pragma unroll
         for (int i = 0; i < VNI; ++i) {
             const int jb = u * UK + VKI * i;
@@ -1435,29 +1444,30 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, int bx, int split
                                   (int64_t)(jb & bs_mask) * a.kv_st_slot) * KVB;
             // streamed once: non-temporal, so the stream does not evict
             // what other workgroups reuse from the L2
-            kr[i] = __builtin_nontemporal_load((const u32x4 *)(kbase + pofs + vlofs));
-            vr[i] = __builtin_nontemporal_load((const u32x4 *)(vbase + pofs + vlofs));
+            kr[SI][i] = __builtin_nontemporal_load((const u32x4 *)(kbase + pofs + vlofs));
+            vr[SI][i] = __builtin_nontemporal_load((const u32x4 *)(vbase + pofs + vlofs));
         }
     };
     uint8_t *const sK = lds + wv * (2 * VST);
     uint8_t *const sV = sK + VST;
-    auto store_kv = [&](int u) {
+    auto store_kv = [&](int u, auto set) {
+        constexpr int SI = decltype(set)::value;
         const bool full = (u + 1) * UK <= kv_end;
 #pragma unroll
         for (int i = 0; i < VNI; ++i) {
             const int row = VKI * i + vkey;
-            u32x4 v = vr[i];
+            u32x4 v = vr[SI][i];
             if (!full && u * UK + row >= kv_end)
                 v = u32x4{0, 0, 0, 0};          // clamped-page keys weigh 0; zero their values
             if constexpr (FP8KV) {
                 // 16 codes = d 16vch .. 16vch+15 -> granules 2vch, 2vch+1
                 const int g0 = 2 * vch;
-                *(u32x4 *)(sK + row * 256 + ((g0 ^ swz_k(row)) << 4)) = widen_fp8<F16>(u32x2{kr[i][0], kr[i][1]});
-                *(u32x4 *)(sK + row * 256 + (((g0 + 1) ^ swz_k(row)) << 4)) = widen_fp8<F16>(u32x2{kr[i][2], kr[i][3]});
+                *(u32x4 *)(sK + row * 256 + ((g0 ^ swz_k(row)) << 4)) = widen_fp8<F16>(u32x2{kr[SI][i][0], kr[SI][i][1]});
+                *(u32x4 *)(sK + row * 256 + (((g0 + 1) ^ swz_k(row)) << 4)) = widen_fp8<F16>(u32x2{kr[SI][i][2], kr[SI][i][3]});
                 *(u32x4 *)(sV + row * 256 + ((g0 ^ swz_v(row)) << 4)) = widen_fp8<F16>(u32x2{v[0], v[1]});
                 *(u32x4 *)(sV + row * 256 + (((g0 + 1) ^ swz_v(row)) << 4)) = widen_fp8<F16>(u32x2{v[2], v[3]});
             } else {
-                *(u32x4 *)(sK + row * 256 + ((vch ^ swz_k(row)) << 4)) = kr[i];
+                *(u32x4 *)(sK + row * 256 + ((vch ^ swz_k(row)) << 4)) = kr[SI][i];
                 *(u32x4 *)(sV + row * 256 + ((vch ^ swz_v(row)) << 4)) = v;
             }
         }
@@ -1468,12 +1478,12 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, int bx, int split
     u32x4 qf[8];
     const float c2 = a.scale_log2 * (FP8KV ? *a.k_scale : 1.0f);
     const uint8_t *krow = sK + swap23(lc) * 256;
-    auto step = [&](int u) {
-        store_kv(u);                            // K, V(u) registers -> this wave's stages
-        if (u + NW < u_end) {                   // ids of u + NW were fetched last step
-            load_kv(u + NW);
-            if (u + 2 * NW < u_end)
-                fetch_ids(u + 2 * NW);
+    auto step = [&](int u, auto set) {
+        store_kv(u, set);                       // K, V(u) registers -> this wave's stages
+        if (u + NSET * NW < u_end) {            // ids of that unit were fetched last step
+            load_kv(u + NSET * NW, set);
+            if (u + (NSET + 1) * NW < u_end)
+                fetch_ids(u + (NSET + 1) * NW);
         }
         auto kf = [&](int b, int ks) {
             return *(const u32x4 *)(krow + 32 * b * 256 + (((2 * ks + hl) ^ (lane & 15)) << 4));
@@ -1486,13 +1496,24 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, int bx, int split
     int u = u_begin + wv;
     if (u < u_end) {
         fetch_ids(u);
-        load_kv(u);
-        if (u + NW < u_end)
-            fetch_ids(u + NW);
+        load_kv(u, S0{});
+        if constexpr (NSET == 2) {
+            if (u + NW < u_end) {
+                fetch_ids(u + NW);
+                load_kv(u + NW, S1{});
+            }
+        }
+        if (u + NSET * NW < u_end)
+            fetch_ids(u + NSET * NW);
     }
     load_q(a, qf, row_ok, tok, head, lane);
-    for (; u < u_end; u += NW)
-        step(u);
+    for (; u < u_end; u += NSET * NW) {
+        step(u, S0{});
+        if constexpr (NSET == 2) {
+            if (u + NW < u_end)
+                step(u + NW, S1{});
+        }
+    }
 
     // merge the waves' states: each wave writes (o, m, l) per lane, then wave
     // w < 4 combines d block w of every row and writes it
@@ -1578,15 +1599,15 @@ void attn_fwd_kernel(const AttnArgs a) {
             if (d >= a.decode_wgs)
                 return;
             const int pair = d / a.num_splits;
-            decode_body<F16, FP8KV, CAUSAL, true, kWaves, EXT>(a, pair, d - pair * a.num_splits, lds);
+            decode_body<F16, FP8KV, CAUSAL, true, kWaves, EXT>(a, pair, d - pair * a.num_splits, (int)threadIdx.x, lds);
         } else {
             const int pi = 8 * (b - c0) + r;
             if (pi >= a.prefill_wgs)
                 return;
             if constexpr (F8MM)
-                prefill_body_f8<F16, CAUSAL, false, 1>(a, pi, 0, lds);
+                prefill_body_f8<F16, CAUSAL, false, 1>(a, pi, 0, (int)threadIdx.x, lds);
             else
-                prefill_body<F16, FP8KV, CAUSAL, false, 1, EXT>(a, pi, 0, lds);
+                prefill_body<F16, FP8KV, CAUSAL, false, 1, EXT>(a, pi, 0, (int)threadIdx.x, lds);
         }
         return;
     }
@@ -1595,26 +1616,37 @@ void attn_fwd_kernel(const AttnArgs a) {
         // (split x (decode, prefill)) grid order, so that items which exit at
         // once do not occupy CUs the working ones are then placed behind
         if (a.persist_items > 0) {
-            for (int it = blockIdx.x; it < a.persist_items; it += gridDim.x) {
+            for (int it = blockIdx.x;; it += gridDim.x) {
+                // the thread index passes through an empty asm each item, so
+                // that the per-lane values the bodies derive from it are not
+                // hoisted out of the loop to hold registers across it
+                using KArgs = const __attribute__((address_space(4))) AttnArgs;
+                KArgs *pk = (KArgs *)__builtin_amdgcn_kernarg_segment_ptr();
+                asm volatile("" : "+s"(pk));
+                const AttnArgs &ai = *(const AttnArgs *)pk;
+                int tid = threadIdx.x;
+                asm volatile("" : "+v"(tid));
+                if (it >= ai.persist_items)
+                    break;
                 __syncthreads();                // every wave is done with the last item's LDS
-                const int y = it / a.row_items, x = it - y * a.row_items;
-                if (x < a.decode_wgs)
-                    decode_body<F16, FP8KV, CAUSAL, SPLIT, kWaves * KG, EXT>(a, x, y, lds);
+                const int y = it / ai.row_items, x = it - y * ai.row_items;
+                if (x < ai.decode_wgs)
+                    decode_body<F16, FP8KV, CAUSAL, SPLIT, kWaves * KG, EXT>(ai, x, y, tid, lds);
                 else if constexpr (F8MM)
-                    prefill_body_f8<F16, CAUSAL, SPLIT, KG>(a, x - a.decode_wgs, y, lds);
+                    prefill_body_f8<F16, CAUSAL, SPLIT, KG>(ai, x - ai.decode_wgs, y, tid, lds);
                 else
-                    prefill_body<F16, FP8KV, CAUSAL, SPLIT, KG, EXT>(a, x - a.decode_wgs, y, lds);
+                    prefill_body<F16, FP8KV, CAUSAL, SPLIT, KG, EXT>(ai, x - ai.decode_wgs, y, tid, lds);
             }
             return;
         }
     }
     const int bx = blockIdx.x;
     if (bx < a.decode_wgs)
-        decode_body<F16, FP8KV, CAUSAL, SPLIT, kWaves * KG, EXT>(a, bx, blockIdx.y, lds);
+        decode_body<F16, FP8KV, CAUSAL, SPLIT, kWaves * KG, EXT>(a, bx, blockIdx.y, (int)threadIdx.x, lds);
     else if constexpr (F8MM)
-        prefill_body_f8<F16, CAUSAL, SPLIT, KG>(a, bx - a.decode_wgs, blockIdx.y, lds);
+        prefill_body_f8<F16, CAUSAL, SPLIT, KG>(a, bx - a.decode_wgs, blockIdx.y, (int)threadIdx.x, lds);
     else
-        prefill_body<F16, FP8KV, CAUSAL, SPLIT, KG, EXT>(a, bx - a.decode_wgs, blockIdx.y, lds);
+        prefill_body<F16, FP8KV, CAUSAL, SPLIT, KG, EXT>(a, bx - a.decode_wgs, blockIdx.y, (int)threadIdx.x, lds);
 }
 
 // ------------------------------------------------------------------ combine kernel
