@@ -1616,18 +1616,26 @@ void attn_fwd_kernel(const AttnArgs a) {
         // (split x (decode, prefill)) grid order, so that items which exit at
         // once do not occupy CUs the working ones are then placed behind
         if (a.persist_items > 0) {
-            for (int it = blockIdx.x;; it += gridDim.x) {
-                // the thread index passes through an empty asm each item, so
-                // that the per-lane values the bodies derive from it are not
-                // hoisted out of the loop to hold registers across it
+            // odd workgroups take their items in reverse order, so that about
+            // half of them start with each kind (streaming decode items
+            // then overlap compute-bound prefill items instead of all
+            // running at the start or at the end)
+            const int n_mine = (a.persist_items - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+            const bool rev = blockIdx.x & 1;
+            for (int k = 0;; ++k) {
+                // the argument pointer (the kernel-argument segment) and the
+                // thread index pass through an empty asm each item, so that the
+                // values the bodies derive from them are not hoisted out of the
+                // loop to hold registers across it
                 using KArgs = const __attribute__((address_space(4))) AttnArgs;
                 KArgs *pk = (KArgs *)__builtin_amdgcn_kernarg_segment_ptr();
                 asm volatile("" : "+s"(pk));
                 const AttnArgs &ai = *(const AttnArgs *)pk;
                 int tid = threadIdx.x;
                 asm volatile("" : "+v"(tid));
-                if (it >= ai.persist_items)
+                if (k >= n_mine)
                     break;
+                const int it = (int)blockIdx.x + (rev ? n_mine - 1 - k : k) * (int)gridDim.x;
                 __syncthreads();                // every wave is done with the last item's LDS
                 const int y = it / ai.row_items, x = it - y * ai.row_items;
                 if (x < ai.decode_wgs)
