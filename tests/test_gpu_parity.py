@@ -275,6 +275,22 @@ def test_split_prefill_two_key_groups(case):
     H.compare(wl, out, lse, what=f"key groups {case}")
 
 
+
+def test_split_prefill_many_items_one_workgroup_each():
+    # a split launch with prefill work and more than 8 x 256 items: one
+    # 8-wave workgroup per item instead of the persistent form (sampled rows,
+    # every decode row)
+    wl = wk.make_paged("manyitems", 5600, [1300, 1, 1100, 900, 2, 1300],
+                       [1400, 700, 1100, 1000, 900, 1500], 16, 16, block_size=16, causal=True)
+    info = H.plan(wl, num_splits=4)
+    assert info.num_waves == 8 and (info.grid_x + info.decode_grid_x) * info.grid_y > 8 * 256
+    H.say(f"split launch with {(info.grid_x + info.decode_grid_x) * info.grid_y} items")
+    out, lse = H.run(wl, num_splits=4)
+    cu = wl.cu_seqlens_q.tolist()
+    dec = [(t, h) for s in (1, 4) for t in range(cu[s], cu[s + 1]) for h in range(16)]
+    rows = np.concatenate([H.sample_rows(wl, 400, seed=56), np.array(dec)])
+    H.compare(wl, out, lse, rows=rows, what="many-item split launch")
+
 # ------------------------------------------------------------------ local attention and ALiBi
 
 MASK_CASES = [
