@@ -360,7 +360,7 @@ def decode_half(args, call, stream) -> dict:
             e1.record(stream)
         torch.cuda.synchronize()
         warm = np.array([a.elapsed_time(b) for a, b in evs])
-        cold = time_calls(fn, 10, stream, flush)
+        cold = time_calls(fn, 50, stream, flush)
         kvb = wl.kv_bytes()
         ach = kvb / (warm.mean() * 1e-3) / 1e9
         res[cfg] = {
@@ -624,7 +624,8 @@ def time_calls(fn, n: int, stream, flush=None):
 
 def extras(args, prepared, per, result, call, stream) -> None:
     """Measurements made after the timed region (they do not enter `value`):
-    per-call times with L2/MALL flushed before each call (a 512 MB write), the
+    per-call times with L2/MALL flushed before each call (a 512 MB write; median
+    and min of 50 calls, after the warm-up and timed calls), the
     decode batch at splits 1/2/4/8, and the mixed batch's prefill-only and
     decode-only sub-batches with its roofline time max(F/P_mfma, B_KV/P_hbm)."""
     import numpy as np
@@ -635,7 +636,7 @@ def extras(args, prepared, per, result, call, stream) -> None:
     scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     flush = lambda: scrub.fill_(1)
     for label, wl, splits, d, ws in prepared:
-        t = time_calls(lambda: call(wl, splits, d, ws), 10, stream, flush)
+        t = time_calls(lambda: call(wl, splits, d, ws), 50, stream, flush)
         per_r = result["per_call"][label]
         per_r["ms_cold_median"] = round(float(np.median(t)), 4)
         per_r["ms_cold_min"] = round(float(t.min()), 4)
