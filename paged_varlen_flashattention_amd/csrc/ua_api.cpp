@@ -150,7 +150,9 @@ Plan make_plan(const ua_attn_params *p) {
     const int G = p->num_q_heads / p->num_kv_heads;
     const bool decode_only = (int64_t)p->max_seqlen_q * G <= ua::kDecodeRows;
     pl.prefill = !decode_only;
-    pl.decode = true;
+    // the decode kernel runs only where some sequence can be a decode
+    // sequence (its workgroups would otherwise all exit at once)
+    pl.decode = decode_only || may_have_decode_rows(p, G);
     pl.block_q = ua::kPrefillBlockM / G;
     pl.qslots = (int64_t)p->num_tokens / pl.block_q + p->num_seqs;
     pl.mix = false;
@@ -158,6 +160,8 @@ Plan make_plan(const ua_attn_params *p) {
     if (splits < 0) {
         splits = -splits;
         pl.mix = pl.prefill;            // decode-only launches: every row is a decode row
+        if (pl.prefill && !pl.decode)
+            splits = 1;                 // no decode rows to split
     }
     if (splits == 0) {
         int64_t units;

@@ -99,9 +99,11 @@ def test_valid_plan_prefill(lib):
     st, info = plan_status(lib, p)
     assert st == 0
     assert (info.block_m, info.block_q, info.tile_n, info.num_waves) == (128, 128, 64, 4)
-    assert info.kernels == 3                                   # prefill + decode (short sequences)
+    # prefill only: T - (S - 1) * max_seqlen_q = 4096 tokens, no sequence can
+    # have q_len * G <= 32, so no decode workgroups are launched
+    assert info.kernels == 1
     assert info.grid_x == (16384 // 128 + 4) * 32
-    assert info.decode_grid_x == 4 * 32
+    assert info.decode_grid_x == 0
 
 
 def test_plan_gqa_block_q(lib):
@@ -286,12 +288,17 @@ def test_plan_no_decode_split_without_decode_rows(lib):
                     kv_stride_block=16 * 32 * 128, kv_stride_slot=32 * 128,
                     workspace=FAKE, workspace_bytes=1 << 40)
     st, info = plan_status(lib, p)
-    assert st == 0 and info.kernels == 3 and info.num_splits == 1
+    assert st == 0 and info.kernels == 1 and info.num_splits == 1
     # the bound T - (S - 1) * max_q <= 32 / G: 33 tokens left for the
     # shortest sequence rule a decode sequence out, 32 do not
     p.num_tokens = 3 * 4096 + 33
     st, info = plan_status(lib, p)
-    assert st == 0 and info.kernels == 3 and info.num_splits == 1
+    assert st == 0 and info.kernels == 1 and info.num_splits == 1 and info.decode_grid_x == 0
+    # an explicit decode-row split of a launch without decode rows runs unsplit
+    p.num_splits = -4
+    st, info = plan_status(lib, p)
+    assert st == 0 and info.kernels == 1 and info.num_splits == 1
+    p.num_splits = 0
     p.num_tokens = 3 * 4096 + 32
     p.max_seqlen_k, p.block_table_stride = 8192, 512
     st, info = plan_status(lib, p)
