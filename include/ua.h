@@ -200,7 +200,10 @@ typedef struct ua_attn_params {
  * share each 64-key tile) and the decode kernel (every sequence with
  * q_len * (Hq / Hkv) <= 32 query rows: 4 waves stream disjoint 32-key units
  * and merge).  When max_seqlen_q * (Hq / Hkv) <= 32 only the decode kernel
- * runs; otherwise both run and the prefill kernel skips the short sequences.
+ * runs.  Otherwise the prefill kernel runs, and the decode kernel runs beside
+ * it (the prefill kernel then skipping the short sequences) only when some
+ * sequence can be short: when num_tokens - (num_seqs - 1) * max_seqlen_q
+ * <= 32 / (Hq / Hkv).
  * Split launches with prefill work use 8-wave workgroups: two groups of 4
  * prefill waves take alternate tiles of the split and merge, and the decode
  * body streams with 8 waves; when such a launch has at most 8 x 256

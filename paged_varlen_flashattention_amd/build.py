@@ -28,16 +28,6 @@ HIPCC_FLAGS = [
     "-Wall", "-Wno-unused-function",
 ]
 
-# Per-source flags.  The attention kernels that run at one wave per SIMD (the
-# 64-row prefill body) keep their MFMA accumulators in ordinary registers and
-# only the query fragments in AccVGPRs; without this the compiler puts every
-# accumulator in AccVGPRs and copies them back and forth around the softmax.
-# The kernels at two waves per SIMD use no AccVGPRs, so it does not change
-# their code.
-SOURCE_FLAGS = {
-    "ua_attention.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"],
-}
-
 
 def hipcc() -> str:
     path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
@@ -54,7 +44,7 @@ def build(verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(objdir, src + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [hipcc(), *HIPCC_FLAGS, *SOURCE_FLAGS.get(src, []), "-I", INCLUDE, "-I", CSRC, *lang, "-c",
+        cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, *lang, "-c",
                os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)

@@ -995,293 +995,6 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, int bx, int spli
     }
 }
 
-// ------------------------------------------------------------------ 64-row prefill
-
-// The mask step of tile_softmax (keys at or past lim get -inf).
-template <int NKB>
-__device__ __forceinline__ void tile_mask(f32x16 (&sacc)[NKB], int key0, int lim, int lane) {
-    const int j0 = key0 + 8 * (lane >> 5);
-#pragma unroll
-    for (int b = 0; b < NKB; ++b)
-#pragma unroll
-        for (int q = 0; q < 16; ++q)
-            if (j0 + 32 * b + 16 * (q >> 3) + (q & 7) >= lim)
-                sacc[b][q] = neg_inf();
-}
-
-// The rest of tile_softmax, on masked scores, without the rescale of the
-// accumulators: returns whether some row moved its reference max (uniform),
-// with alpha the factor that row's accumulators must then be multiplied by
-// before the tile's PV product (1 for the other rows).  m and l are updated
-// here, so the caller only defers the accumulator multiply, past MFMA work of
-// another row block; no branch inside, so the caller can place it in one
-// basic block with such MFMA work.
-template <bool F16, int NKB>
-__device__ __forceinline__ bool tile_weights(RowState &st, f32x16 (&sacc)[NKB], u32x4 (&pf)[2 * NKB],
-                                             float &alpha, float c2) {
-    float mx = neg_inf();
-#pragma unroll
-    for (int b = 0; b < NKB; ++b)
-#pragma unroll
-        for (int q = 0; q < 16; ++q)
-            mx = fmaxf(mx, sacc[b][q]);
-    mx = xhalf_max(mx);
-    const float tmax = mx * c2;
-    const bool grow = tmax > st.m + kRescaleLog2;
-    alpha = grow ? __builtin_amdgcn_exp2f(st.m - tmax) : 1.0f;   // 0 if m was -inf
-    st.m = grow ? tmax : st.m;
-    st.l *= alpha;
-    const float m_use = (st.m == neg_inf()) ? 0.0f : st.m;
-    float rs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int b = 0; b < NKB; ++b)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[b][q], c2, -m_use));
-            sacc[b][q] = p;
-            if constexpr (!F16)
-                rs[q & 3] += p;
-        }
-#pragma unroll
-    for (int b = 0; b < NKB; ++b)
-#pragma unroll
-        for (int hsel = 0; hsel < 2; ++hsel) {
-            const int q0 = 8 * hsel;
-            if constexpr (F16) {
-                const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
-                f16x2 h[4];
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    h[w] = f16x2{(_Float16)sacc[b][q0 + 2 * w], (_Float16)sacc[b][q0 + 2 * w + 1]};
-                    rs[w] = __builtin_amdgcn_fdot2(h[w], ones, rs[w], false);
-                }
-                pf[2 * b + hsel] = u32x4{__builtin_bit_cast(uint32_t, h[0]), __builtin_bit_cast(uint32_t, h[1]),
-                                         __builtin_bit_cast(uint32_t, h[2]), __builtin_bit_cast(uint32_t, h[3])};
-            } else {
-                pf[2 * b + hsel] = u32x4{pack2<F16>(sacc[b][q0 + 0], sacc[b][q0 + 1]),
-                                         pack2<F16>(sacc[b][q0 + 2], sacc[b][q0 + 3]),
-                                         pack2<F16>(sacc[b][q0 + 4], sacc[b][q0 + 5]),
-                                         pack2<F16>(sacc[b][q0 + 6], sacc[b][q0 + 7])};
-            }
-        }
-    st.l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
-    return __ballot(grow) != 0;
-}
-
-// Prefill workgroup of two waves x 64 rows: each wave holds two 32-row MFMA
-// blocks (rows 64w .. 64w+31 and 64w+32 .. 64w+63 of the 128-row query
-// block), so every K or V fragment it reads from LDS feeds the MFMAs of both,
-// half the LDS reads per flop of prefill_body.  One wave per SIMD (the 512
-// registers hold both blocks' accumulators): within the wave, the second
-// block's score MFMAs run under the first block's softmax and the first
-// block's PV MFMAs under the second block's softmax.  Same query blocks,
-// tiler, LDS stages and swizzles as prefill_body; each wave fills 32 keys of a
-// tile by direct loads, as two 16-key runs (a page holds >= 16 keys).  For
-// unsplit launches without decode workgroups, 16-bit caches and no window or
-// ALiBi.
-template <bool F16, bool CAUSAL>
-__device__ __forceinline__ void prefill_body_r64(const AttnArgs &a, int bx, uint8_t *lds) {
-    constexpr int TN = 64;
-    constexpr int NKB = TN / 32;
-    constexpr int STAGE = 2 * TN * 256;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int hl = lane >> 5;
-    const int lc = lane & 31;
-    uint8_t *const sK0 = lds;
-    uint8_t *const sV0 = sK0 + TN * 256;
-    uint8_t *const sK1 = sK0 + STAGE;
-    uint8_t *const sV1 = sK1 + TN * 256;
-
-    PrefillBlock B;
-    if (!locate_block<CAUSAL, false, false>(a, bx, 0, TN, B))
-        return;
-    const int kvh = B.kvh, s = B.s, cu0 = B.cu0, tq0 = B.tq0, tq1 = B.tq1;
-    const int kv_len = B.kv_len, ctx = B.ctx, kv_end = B.kv_end, n_full = B.n_full;
-    const int t_begin = B.t_begin, n_it = B.t_end - B.t_begin;
-    const int G = a.group;
-
-    // rows of the two blocks
-    u32x4 qf[2][8];
-    RowState st[2];
-    int lim[2];
-    bool row_ok[2];
-    int64_t tok[2];
-    int head[2];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-        const int r = 64 * wv + 32 * rb + lc;
-        const int tq = r / G;
-        const int t_loc = tq0 + tq;
-        row_ok[rb] = t_loc < tq1;
-        tok[rb] = (int64_t)cu0 + t_loc;
-        head[rb] = kvh * G + (r - tq * G);
-        lim[rb] = !row_ok[rb] ? 0 : (CAUSAL ? min(kv_len, ctx + t_loc + 1) : kv_len);
-        load_q(a, qf[rb], row_ok[rb], tok[rb], head[rb], lane);
-        init_rows(st[rb]);
-    }
-    // the query fragments are only ever MFMA operands: they move to AccVGPRs
-    // (which the MFMAs read directly), leaving the ordinary registers to the
-    // accumulators, scores and weights
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                uint32_t v = qf[rb][ks][e];
-                asm volatile("v_accvgpr_write_b32 %0, %1" : "=a"(v) : "v"(v));
-                qf[rb][ks][e] = v;
-            }
-    const bool wave_on = 64 * wv < (tq1 - tq0) * G;      // uniform
-
-    // paging
-    const int32_t *btrow = a.block_table + (int64_t)s * a.bt_stride;
-    const int lbs = a.log2_block_size;
-    const int bs_mask = (1 << lbs) - 1;
-    const int last_page = (max(kv_end, 1) - 1) >> lbs;
-    const uint8_t *kbase = (const uint8_t *)a.k + (int64_t)kvh * a.kv_st_head * 2;
-    const uint8_t *vbase = (const uint8_t *)a.v + (int64_t)kvh * a.kv_st_head * 2;
-    const float c2 = a.scale_log2;
-
-    // one 64-key tile: the same arithmetic, in the same order, as
-    // prefill_body's attend_tile (scores, one softmax step over the 64 keys,
-    // PV) for each row block, so that a row's result does not depend on which
-    // of the two bodies ran it; every K and V fragment read feeds both blocks
-    auto compute = [&](int tile, const uint8_t *sK, bool masked) {
-        const uint8_t *sV = sK + TN * 256;
-        const uint8_t *krow = sK + swap23(lc) * 256;
-        const int key0 = tile * TN;
-        f32x16 sa[NKB], sb[NKB];
-#pragma unroll
-        for (int b = 0; b < NKB; ++b) {
-            sa[b] = f32x16{};
-            sb[b] = f32x16{};
-        }
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-            for (int b = 0; b < NKB; ++b) {
-                const u32x4 kf = *(const u32x4 *)(krow + 32 * b * 256 + (((2 * ks + hl) ^ (lane & 15)) << 4));
-                sa[b] = mfma32<F16>(kf, qf[0][ks], sa[b]);
-                sb[b] = mfma32<F16>(kf, qf[1][ks], sb[b]);
-            }
-        u32x4 pa[2 * NKB], pb[2 * NKB];
-        float alpha_a, alpha_b;
-        if (masked) {
-            tile_mask<NKB>(sa, key0, lim[0], lane);
-            tile_mask<NKB>(sb, key0, lim[1], lane);
-        }
-        if (tile_weights<F16, NKB>(st[0], sa, pa, alpha_a, c2)) {
-#pragma unroll
-            for (int x = 0; x < 4; ++x)
-                st[0].o[x] *= alpha_a;
-        }
-        if (tile_weights<F16, NKB>(st[1], sb, pb, alpha_b, c2)) {
-#pragma unroll
-            for (int x = 0; x < 4; ++x)
-                st[1].o[x] *= alpha_b;
-        }
-#pragma unroll
-        for (int kk = 0; kk < 2 * NKB; ++kk)
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const u32x4 vf = vfrag_lds(sV, kk, x, lane);
-                st[0].o[x] = mfma32<F16>(vf, pa[kk], st[0].o[x]);
-                st[1].o[x] = mfma32<F16>(vf, pb[kk], st[1].o[x]);
-            }
-    };
-
-    // direct loads: wave w fills keys 32w .. 32w+31 of a tile, as two 16-key
-    // runs h (each within one page, its id a scalar load a tile ahead), four
-    // 4-key instructions per run and tensor
-    const int lrow = lane >> 4;
-    uint32_t koff[4], voff[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t rofs = (uint32_t)((4 * i + lrow) * a.kv_st_slot * 2);
-        koff[i] = rofs + (uint32_t)(((lane & 15) ^ swz_k(4 * i + lrow)) << 4);
-        voff[i] = rofs + (uint32_t)(((lane & 15) ^ swz_v(lrow)) << 4);
-    }
-    const int wrow = 32 * wv;
-    const uint32_t lds_row0 = (uint32_t)reinterpret_cast<uintptr_t>(
-        (__attribute__((address_space(3))) uint8_t *)(sK0)) + (uint32_t)(wrow * 256);
-    int32_t blk0 = 0, blk1 = 0;
-    auto fetch_id = [&](int tile) {
-        const int j = tile * TN + wrow;
-        blk0 = sload(btrow + min(j >> lbs, last_page));
-        blk1 = sload(btrow + min((j + 16) >> lbs, last_page));
-    };
-    auto dma_run = [&](const uint8_t *gk, const uint8_t *gv, uint32_t base, auto kofs, auto vofs) {
-        constexpr int KO = decltype(kofs)::value, VO = decltype(vofs)::value;
-        lds_dma16_at<KO + 0 * 256>(gk, koff[0], base);
-        lds_dma16_at<VO + 0 * 256>(gv, voff[0], base);
-        lds_dma16_at<KO + 4 * 256>(gk, koff[1], base);
-        lds_dma16_at<VO + 4 * 256>(gv, voff[1], base);
-        lds_dma16_at<KO + 8 * 256>(gk, koff[2], base);
-        lds_dma16_at<VO + 8 * 256>(gv, voff[2], base);
-        lds_dma16_at<KO + 12 * 256>(gk, koff[3], base);
-        lds_dma16_at<VO + 12 * 256>(gv, voff[3], base);
-    };
-    // stg: the LDS stage (0 or 1) the tile goes to
-    auto dma_tile = [&](int tile, int stg) {
-        const uint32_t base = lds_row0 + (uint32_t)(stg * STAGE);
-        const int j = tile * TN + wrow;
-        const int64_t p0 = ((int64_t)blk0 * a.kv_st_blk + (int64_t)(j & bs_mask) * a.kv_st_slot) * 2;
-        const int64_t p1 = ((int64_t)blk1 * a.kv_st_blk + (int64_t)((j + 16) & bs_mask) * a.kv_st_slot) * 2;
-        dma_run(kbase + p0, vbase + p0, base, std::integral_constant<int, 0>{},
-                std::integral_constant<int, TN * 256>{});
-        dma_run(kbase + p1, vbase + p1, base, std::integral_constant<int, 16 * 256>{},
-                std::integral_constant<int, TN * 256 + 16 * 256>{});
-    };
-    auto zero_tail = [&](int tile, uint8_t *sV) {
-        if ((tile + 1) * TN > kv_end) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                if (tile * TN + wrow + 4 * i + lrow >= kv_end)
-                    *(u32x4 *)(sV + (wrow + 4 * i) * 256 + 16 * lane) = u32x4{0, 0, 0, 0};
-        }
-    };
-    if (n_it > 0) {
-        fetch_id(t_begin);
-        dma_tile(t_begin, 0);
-        if (n_it > 1)
-            fetch_id(t_begin + 1);
-        wait_vmem();
-        zero_tail(t_begin, sV0);
-        __syncthreads();
-    }
-    // one tile per iteration (not unrolled by stage: a single copy of the
-    // loop body keeps the accumulators' live ranges simple); tile k + 1 is
-    // loaded into the other stage during the compute of tile k
-    for (int k = 0; k < n_it; ++k) {
-        const int cur = k & 1;
-        if (k + 1 < n_it) {
-            dma_tile(t_begin + k + 1, cur ^ 1);
-            if (k + 2 < n_it)
-                fetch_id(t_begin + k + 2);
-        }
-        if (wave_on)
-            compute(t_begin + k, sK0 + cur * STAGE, t_begin + k >= n_full);
-        if (k + 1 < n_it) {
-            wait_vmem();
-            zero_tail(t_begin + k + 1, sV0 + (cur ^ 1) * STAGE);
-            __syncthreads();
-        }
-    }
-
-    if (!wave_on)
-        return;
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-        const float l_row = xhalf_sum(st[rb].l);
-        if (row_ok[rb])
-            write_rows<F16, false, 4>(a, st[rb].o, 0, st[rb].m, l_row, 1.0f, tok[rb], head[rb], 0, lane,
-                                      true);
-    }
-}
-
 // ------------------------------------------------------------------ fp8-MFMA prefill
 
 // Opt-in fp8 compute for fp8 caches (the fp8 attention variants of page
@@ -1968,15 +1681,6 @@ void attn_fwd_kernel(const AttnArgs a) {
                                                          (int)threadIdx.x, lds);
 }
 
-// Unsplit launches without decode workgroups, 16-bit caches, no window or
-// ALiBi: two 64-row waves per 128-row query block, one wave per SIMD.
-template <bool F16, bool CAUSAL>
-__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void attn_fwd_r64_kernel(const AttnArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * 2 * 64 * 256];
-    prefill_body_r64<F16, CAUSAL>(a, (int)blockIdx.x, lds);
-}
-
 // ------------------------------------------------------------------ combine kernel
 
 // One wave per row.  Lane = (split group sg = lane / 16, d chunk c = lane % 16,
@@ -2104,25 +1808,9 @@ hipError_t launch_shape(const AttnArgs &a, bool split, bool wide, bool mix, dim3
                 : launch_kernel<F16, FP8KV, CAUSAL, true, 1, EXT, F8MM>(a, grid, st);
 }
 
-// The 64-row body measured slower than the 4-wave one on every workload
-// (dense fp16 full call 1.33 ms against 1.15), so it is not launched unless
-// the library is built with UA_R64=1.
-#ifndef UA_R64
-#define UA_R64 0
-#endif
 template <bool F16, bool FP8KV>
 hipError_t launch_mode(const AttnArgs &a, bool causal, bool split, bool wide, bool mix, bool ext,
                        dim3 grid, hipStream_t st) {
-    if constexpr (!FP8KV) {
-        if (UA_R64 && !split && !mix && !ext && a.decode_wgs == 0 && a.short_to_decode == 0) {
-            (void)hipGetLastError();
-            if (causal)
-                hipLaunchKernelGGL((attn_fwd_r64_kernel<F16, true>), grid, dim3(128), 0, st, a);
-            else
-                hipLaunchKernelGGL((attn_fwd_r64_kernel<F16, false>), grid, dim3(128), 0, st, a);
-            return hipGetLastError();
-        }
-    }
     if constexpr (FP8KV) {
         if (a.fp8_compute) {
             if (ext)
