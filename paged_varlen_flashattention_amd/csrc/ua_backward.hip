@@ -41,6 +41,7 @@
 #include "ua_internal.h"
 
 #include <hip/hip_runtime.h>
+#include <type_traits>
 #include <stdint.h>
 
 namespace ua {
@@ -323,17 +324,26 @@ void bwd_dkdv_kernel(const BwdArgs a) {
         }
         const bool masked = r0 + kRT > ql || (CAUSAL && kw0 + 31 > ctx + r0);
         float p[16], ds[16];
+        // the tile-level test chooses between two straight copies of the
+        // elementwise step (a uniform test inside the loop became a branch
+        // per element)
+        auto weights = [&](auto masked_c) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            float pv = __builtin_amdgcn_exp2f(sc[i] * c2 - lv[i]);
-            if (masked) {
-                const int r = r0 + 16 * (i >> 3) + 8 * hl + (i & 7);
-                if (r >= ql || (CAUSAL && myk > ctx + r))
-                    pv = 0.0f;
+            for (int i = 0; i < 16; ++i) {
+                float pv = __builtin_amdgcn_exp2f(sc[i] * c2 - lv[i]);
+                if constexpr (decltype(masked_c)::value) {
+                    const int r = r0 + 16 * (i >> 3) + 8 * hl + (i & 7);
+                    if ((r >= ql) | (CAUSAL & (myk > ctx + r)))   // no short-circuit branch
+                        pv = 0.0f;
+                }
+                p[i] = pv;
+                ds[i] = pv * (dp[i] - dv[i]);
             }
-            p[i] = pv;
-            ds[i] = pv * (dp[i] - dv[i]);
-        }
+        };
+        if (masked)
+            weights(std::true_type{});
+        else
+            weights(std::false_type{});
         u32x4 pp[2], dd[2];
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
@@ -506,16 +516,23 @@ void bwd_dq_kernel(const BwdArgs a) {
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
             float ds[16];
+            // two straight copies of the elementwise step, chosen per tile
+            auto weights = [&](auto masked_c) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float pv = __builtin_amdgcn_exp2f(sc[b][i] * c2 - lse2);
-                if (masked) {
-                    const int j = t * kTN + 32 * b + 16 * (i >> 3) + 8 * hl + (i & 7);
-                    if (j >= lim)
-                        pv = 0.0f;
+                for (int i = 0; i < 16; ++i) {
+                    float pv = __builtin_amdgcn_exp2f(sc[b][i] * c2 - lse2);
+                    if constexpr (decltype(masked_c)::value) {
+                        const int j = t * kTN + 32 * b + 16 * (i >> 3) + 8 * hl + (i & 7);
+                        if (j >= lim)
+                            pv = 0.0f;
+                    }
+                    ds[i] = pv * (dp[b][i] - delta);
                 }
-                ds[i] = pv * (dp[b][i] - delta);
-            }
+            };
+            if (masked)
+                weights(std::true_type{});
+            else
+                weights(std::false_type{});
 #pragma unroll
             for (int c = 0; c < 2; ++c)
                 dd[2 * b + c] = u32x4{pk2<F16>(ds[8 * c], ds[8 * c + 1]), pk2<F16>(ds[8 * c + 2], ds[8 * c + 3]),
