@@ -32,9 +32,27 @@ def test_config1_tiny_paged_varlen():
 @pytest.mark.parametrize("causal", [True, False])
 def test_config2_dense_reduced_all_rows(causal):
     wl = wk.config2(causal=causal, batch=2, heads=4, seq=640)
+    info = H.plan(wl)
+    assert info.kernels & 2 == 0 and info.decode_grid_x == 0, info.as_dict()   # no decode workgroups
     H.say(f"config2 reduced causal={causal}")
     out, lse = H.run(wl)
     H.compare(wl, out, lse, what="config2 reduced")
+
+
+@pytest.mark.parametrize("q_short,decode_kernel", [(9, False), (8, True)])
+def test_decode_kernel_only_when_short_sequences_possible(q_short, decode_kernel):
+    # G = 4, q_lens [40, q_short]: the shortest sequence has at least
+    # T - (S - 1) * max_seqlen_q = q_short tokens, so the decode kernel runs
+    # only when q_short * G <= 32 is possible (8 tokens: 32 rows, a decode
+    # sequence); with 9 tokens (36 rows) the prefill kernel takes both
+    wl = wk.make_paged("decode-rule", 5100 + q_short, [40, q_short], [300, 77], 8, 2, block_size=16,
+                       causal=True)
+    info = H.plan(wl, num_splits=1)
+    assert bool(info.kernels & 2) == decode_kernel, info.as_dict()
+    assert (info.decode_grid_x > 0) == decode_kernel, info.as_dict()
+    H.say(f"decode kernel rule q_short={q_short}")
+    out, lse = H.run(wl, num_splits=1)
+    H.compare(wl, out, lse, what=f"decode rule {q_short}")
 
 
 @pytest.mark.parametrize("causal", [True, False])
