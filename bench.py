@@ -482,8 +482,9 @@ def bwd_flops(q_lens, k_lens, heads: int, causal: bool, D: int = 128) -> float:
 
 def main_bwd(args) -> None:
     """Attention backward on the backward benchmark shape: O and LSE from one
-    (untimed) HIP forward; a step is one ua_attention_backward call (Delta
-    preprocess, dK/dV kernel, dQ kernel).  Value: algorithmic TFLOP/s."""
+    (untimed) HIP forward; a step is one ua_attention_backward call (the dQ
+    kernel, which also forms Delta, then the dK/dV kernel).  Value: algorithmic
+    TFLOP/s."""
     import numpy as np
     import torch
 
@@ -539,7 +540,7 @@ def main_bwd(args) -> None:
         "roofline": {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(ach / PEAK_MFMA_TFLOPS, 4), "traffic": traffic_from_profiles("bwd_call"),
                      "launch_ms_mean": round(float(durs.mean()), 4),
-                     "kernel": "one ua_attention_backward call (preprocess + dK/dV + dQ kernels)"},
+                     "kernel": "one ua_attention_backward call (dQ + dK/dV kernels)"},
         "per_call": {"backward": {"ms_mean": round(float(durs.mean()), 4), "ms_min": round(float(durs.min()), 4),
                                   "ms_median": round(float(np.median(durs)), 4), "flops": flops}},
     }

@@ -9,20 +9,21 @@
 //   dQ = scale * dS K,  dK = scale * dS^T Q,
 // with a kv head's dK and dV summed over the query heads that read it.
 //
-// Three kernels, launched in order on one stream:
-//   * bwd_prep_kernel: Delta and LSE * log2(e) of every (token, head) row,
-//     written head-major ([Hq][T]) into the workspace so that 32 consecutive
-//     rows of one head are 128 contiguous bytes (rows that see no key get
-//     +inf, so that their P is exp2(-inf) = 0);
+// Two kernels, launched in order on one stream:
+//   * bwd_dq_kernel: one 4-wave workgroup per (sequence, kv head, block of
+//     128 / G query tokens x the G heads), each wave 32 rows with Q and dO in
+//     registers, streaming 64-key K and V tiles through LDS as in the forward.
+//     It also forms Delta (from the row's O and the dO it holds) and
+//     LSE * log2(e) of each of its rows and writes them head-major ([Hq][T])
+//     into the workspace, so that 32 consecutive rows of one head are 128
+//     contiguous bytes for the second kernel (rows that see no key get +inf,
+//     so that their P is exp2(-inf) = 0);
 //   * bwd_dkdv_kernel: one 4-wave workgroup per (sequence, kv head, block of
 //     128 keys); wave w keeps the K and V rows of its 32 keys in registers as
 //     MFMA operands and accumulates dK^T and dV^T (32 keys x 128 d) over every
 //     query head of the group and every 32-row query tile that sees its keys.
 //     The Q and dO tiles, and their LSE and Delta, go straight from HBM into
-//     LDS (global_load_lds), double-buffered, one barrier per tile;
-//   * bwd_dq_kernel: one 4-wave workgroup per (sequence, kv head, block of
-//     128 / G query tokens x the G heads), each wave 32 rows with Q and dO in
-//     registers, streaming 64-key K and V tiles through LDS as in the forward.
+//     LDS (global_load_lds), double-buffered, one barrier per tile.
 // The two main kernels recompute S and dP each (seven 128-deep products per
 // (row, key) pair instead of five); in exchange neither needs atomics.
 //
@@ -174,34 +175,6 @@ __device__ __forceinline__ int find_seq(const int32_t *cu, int num_seqs, int B, 
             hi = mid - 1;
     }
     return lo;
-}
-
-// ------------------------------------------------------------------ preprocess
-
-// 16 lanes per (token, head) row, 8 values each; rows = T * Hq.
-template <bool F16>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdArgs a) {
-    const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-    const int part = threadIdx.x & 15;
-    const int64_t rows = (int64_t)a.num_tokens * a.num_q_heads;
-    float acc = 0.0f;
-    if (row < rows) {
-        const u32x4 o = *(const u32x4 *)((const uint8_t *)a.o + row * kRowBytes + 16 * part);
-        const u32x4 g = *(const u32x4 *)((const uint8_t *)a.dout + row * kRowBytes + 16 * part);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            acc += lo16<F16>(o[e]) * lo16<F16>(g[e]) + hi16<F16>(o[e]) * hi16<F16>(g[e]);
-    }
-#pragma unroll
-    for (int m = 8; m >= 1; m >>= 1)
-        acc += __shfl_xor(acc, m, 16);
-    if (row < rows && part == 0) {
-        const int t = (int)(row / a.num_q_heads), h = (int)(row % a.num_q_heads);
-        const int64_t at = (int64_t)h * a.num_tokens + t;
-        const float l = a.lse[row];
-        a.lse2[at] = l == -__builtin_inff() ? __builtin_inff() : l * kLog2eB;
-        a.delta[at] = acc;
-    }
 }
 
 // ------------------------------------------------------------------ dK, dV
@@ -453,13 +426,38 @@ void bwd_dq_kernel(const BwdArgs a) {
             qf[ks] = *(const u32x4 *)(qp + (16 * ks + 8 * hl) * 2);
             df[ks] = *(const u32x4 *)(dp + (16 * ks + 8 * hl) * 2);
         }
-        lse2 = a.lse2[(int64_t)head * a.num_tokens + tok];
-        delta = a.delta[(int64_t)head * a.num_tokens + tok];
     } else {
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
             qf[ks] = u32x4{0, 0, 0, 0};
             df[ks] = u32x4{0, 0, 0, 0};
+        }
+    }
+    // Delta = sum_d O dO of the row: each lane half holds the dO values of
+    // half the row's d (8 per k-step), the matching O values are read here;
+    // LSE * log2(e) from the forward's natural-log LSE.  Both go to the
+    // workspace for the dK/dV kernel (one lane per row).
+    {
+        float part = 0.0f;
+        if (row_ok) {
+            const uint8_t *op = (const uint8_t *)a.o + (tok * Hq + head) * kRowBytes;
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                const u32x4 o = *(const u32x4 *)(op + (16 * ks + 8 * hl) * 2);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    part += lo16<F16>(o[e]) * lo16<F16>(df[ks][e]) + hi16<F16>(o[e]) * hi16<F16>(df[ks][e]);
+            }
+        }
+        const float dsum = part + __shfl_xor(part, 32);     // the other lane half of the row
+        if (row_ok) {
+            const float l = a.lse[tok * Hq + head];
+            lse2 = l == -__builtin_inff() ? __builtin_inff() : l * kLog2eB;
+            delta = dsum;
+            if (hl == 0) {
+                a.lse2[(int64_t)head * a.num_tokens + tok] = lse2;
+                a.delta[(int64_t)head * a.num_tokens + tok] = delta;
+            }
         }
     }
 
@@ -586,21 +584,16 @@ void bwd_dq_kernel(const BwdArgs a) {
 
 template <bool F16, bool CAUSAL>
 hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
-    const int64_t rows = (int64_t)a.num_tokens * a.num_q_heads;
     hipError_t e = hipSuccess;
     (void)hipGetLastError();                    // report these launches' status only
-    if (rows > 0) {
-        hipLaunchKernelGGL((bwd_prep_kernel<F16>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, st, a);
+    // dQ first: it writes the Delta and LSE * log2(e) rows dK/dV reads
+    if (a.dq_wgs > 0) {
+        hipLaunchKernelGGL((bwd_dq_kernel<F16, CAUSAL>), dim3((unsigned)a.dq_wgs), dim3(256), 0, st, a);
         if ((e = hipGetLastError()) != hipSuccess)
             return e;
     }
     if (a.dkdv_wgs > 0) {
         hipLaunchKernelGGL((bwd_dkdv_kernel<F16, CAUSAL>), dim3((unsigned)a.dkdv_wgs), dim3(256), 0, st, a);
-        if ((e = hipGetLastError()) != hipSuccess)
-            return e;
-    }
-    if (a.dq_wgs > 0) {
-        hipLaunchKernelGGL((bwd_dq_kernel<F16, CAUSAL>), dim3((unsigned)a.dq_wgs), dim3(256), 0, st, a);
         e = hipGetLastError();
     }
     return e;

@@ -138,7 +138,7 @@ struct BwdArgs {
     float scale;
 };
 
-// Enqueue the three backward kernels (preprocess, dK/dV, dQ) on stream.
+// Enqueue the two backward kernels (dQ, which also forms Delta, then dK/dV) on stream.
 hipError_t launch_backward(const BwdArgs &a, bool f16, bool causal, hipStream_t stream);
 
 }  // namespace ua
