@@ -480,7 +480,7 @@ __device__ __forceinline__ void attend_tile(RowState &st, const u32x4 (&qf)[8], 
 // rescale threshold (rare after the first tiles), the tile's scores of those
 // rows are shifted by the growth and their bias is rewritten; otherwise the
 // same steps as tile_softmax.
-template <int NKB>
+template <bool F16, int NKB>
 __device__ __forceinline__ void tile_softmax_biased(RowState &st, f32x16 &bias, f32x16 (&sacc)[NKB],
                                                     u32x4 (&pf)[2 * NKB], int key0, bool masked, int lim,
                                                     int lane) {
@@ -526,55 +526,69 @@ __device__ __forceinline__ void tile_softmax_biased(RowState &st, f32x16 &bias, 
         for (int q = 0; q < 16; ++q)
             bias[q] = nb;
     }
+    // weights, the 16-bit B operand and the row sum, as in tile_softmax
     float rs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int b = 0; b < NKB; ++b)
 #pragma unroll
-        for (int q = 0; q < 16; ++q)
-            sacc[b][q] = __builtin_amdgcn_exp2f(sacc[b][q]);
+        for (int q = 0; q < 16; ++q) {
+            const float p = __builtin_amdgcn_exp2f(sacc[b][q]);
+            sacc[b][q] = p;
+            if constexpr (!F16)
+                rs[q & 3] += p;
+        }
 #pragma unroll
     for (int b = 0; b < NKB; ++b)
 #pragma unroll
         for (int hsel = 0; hsel < 2; ++hsel) {
             const int q0 = 8 * hsel;
-            const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
-            f16x2 h[4];
+            if constexpr (F16) {
+                const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+                f16x2 h[4];
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                h[w] = f16x2{(_Float16)sacc[b][q0 + 2 * w], (_Float16)sacc[b][q0 + 2 * w + 1]};
-                rs[w] = __builtin_amdgcn_fdot2(h[w], ones, rs[w], false);
+                for (int w = 0; w < 4; ++w) {
+                    h[w] = f16x2{(_Float16)sacc[b][q0 + 2 * w], (_Float16)sacc[b][q0 + 2 * w + 1]};
+                    rs[w] = __builtin_amdgcn_fdot2(h[w], ones, rs[w], false);
+                }
+                pf[2 * b + hsel] = u32x4{__builtin_bit_cast(uint32_t, h[0]), __builtin_bit_cast(uint32_t, h[1]),
+                                         __builtin_bit_cast(uint32_t, h[2]), __builtin_bit_cast(uint32_t, h[3])};
+            } else {
+                pf[2 * b + hsel] = u32x4{pack2<F16>(sacc[b][q0 + 0], sacc[b][q0 + 1]),
+                                         pack2<F16>(sacc[b][q0 + 2], sacc[b][q0 + 3]),
+                                         pack2<F16>(sacc[b][q0 + 4], sacc[b][q0 + 5]),
+                                         pack2<F16>(sacc[b][q0 + 6], sacc[b][q0 + 7])};
             }
-            pf[2 * b + hsel] = u32x4{__builtin_bit_cast(uint32_t, h[0]), __builtin_bit_cast(uint32_t, h[1]),
-                                     __builtin_bit_cast(uint32_t, h[2]), __builtin_bit_cast(uint32_t, h[3])};
         }
     st.l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
 }
 
-// attend_tile for fp16 with pre-scaled queries and biased score chains
-// (tile_softmax_biased); K fragments read ahead of the chain.
-template <int NKB, class KF, class VF>
+// attend_tile with pre-scaled queries and biased score chains
+// (tile_softmax_biased).  HOIST: K fragments read ahead of the chain, as in
+// tile_scores.
+template <bool F16, int NKB, bool HOIST, class KF, class VF>
 __device__ __forceinline__ void attend_tile_biased(RowState &st, f32x16 &bias, const u32x4 (&qf)[8], KF kfrag,
                                                    VF vfrag, int key0, bool masked, int lim, int lane) {
     f32x16 sacc[NKB];
     u32x4 pf[2 * NKB];
-    u32x4 kall[8][NKB];
+    u32x4 kall[HOIST ? 8 : 1][HOIST ? NKB : 1];
+    if constexpr (HOIST) {
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+            for (int b = 0; b < NKB; ++b)
+                kall[ks][b] = kfrag(b, ks);
+    }
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
-        for (int b = 0; b < NKB; ++b)
-            kall[ks][b] = kfrag(b, ks);
-    __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int b = 0; b < NKB; ++b)
-        sacc[b] = mfma32<true>(kall[0][b], qf[0], bias);
-#pragma unroll
-    for (int ks = 1; ks < 8; ++ks)
-#pragma unroll
-        for (int b = 0; b < NKB; ++b)
-            sacc[b] = mfma32<true>(kall[ks][b], qf[ks], sacc[b]);
+        for (int b = 0; b < NKB; ++b) {
+            const u32x4 kf = HOIST ? kall[HOIST ? ks : 0][HOIST ? b : 0] : kfrag(b, ks);
+            sacc[b] = mfma32<F16>(kf, qf[ks], ks == 0 ? bias : sacc[b]);
+        }
     __builtin_amdgcn_s_setprio(0);
-    tile_softmax_biased<NKB>(st, bias, sacc, pf, key0, masked, lim, lane);
-    tile_pv<true, NKB>(st, pf, vfrag);
+    tile_softmax_biased<F16, NKB>(st, bias, sacc, pf, key0, masked, lim, lane);
+    tile_pv<F16, NKB>(st, pf, vfrag);
 }
 
 // V^T fragment from a row-major [keys][128] LDS V tile with the swz_v layout,
@@ -827,20 +841,30 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, int bx, int spli
     const bool wave_on = wv * 32 < (tq1 - tq0) * G;       // uniform over the wave
     u32x4 qf[8];
     load_q(a, qf, row_ok, tok, head, lane);
-    // fp16 with a 16-bit cache, one key group, no window or ALiBi: the score
-    // chains start from the row's reference (tile_softmax_biased), with the
-    // query rows scaled by the score scale once here (each element rounded
-    // to fp16 once more)
-    constexpr bool biased = F16 && !FP8KV && KG == 1 && !EXT;
+    // fp16 queries without a window or ALiBi: the score chains start from
+    // the row's reference (tile_softmax_biased), with the query rows scaled
+    // by the score scale (and an fp8 cache's K scale) once here, each element
+    // rounded to fp16 once more.  Not for bf16: that rounding (2^-9) moves
+    // the log-sum-exp by about 1e-3.
+    constexpr bool biased = F16 && !EXT;
     f32x16 bias = f32x16{};
     if constexpr (biased) {
+        const float cq = a.scale_log2 * (FP8KV ? *a.k_scale : 1.0f);
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
-            f16x8 h = __builtin_bit_cast(f16x8, qf[ks]);
+            if constexpr (F16) {
+                f16x8 h = __builtin_bit_cast(f16x8, qf[ks]);
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                h[e] = (_Float16)((float)h[e] * a.scale_log2);
-            qf[ks] = __builtin_bit_cast(u32x4, h);
+                for (int e = 0; e < 8; ++e)
+                    h[e] = (_Float16)((float)h[e] * cq);
+                qf[ks] = __builtin_bit_cast(u32x4, h);
+            } else {
+                bf16x8 h = __builtin_bit_cast(bf16x8, qf[ks]);
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    h[e] = (__bf16)((float)h[e] * cq);
+                qf[ks] = __builtin_bit_cast(u32x4, h);
+            }
         }
     }
 
@@ -867,7 +891,7 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, int bx, int spli
         // the ALiBi path measured about 1 % slower with it)
         constexpr bool hoist = F16 && !FP8KV && KG == 1 && !EXT;
         if constexpr (biased)
-            attend_tile_biased<NKB>(st, bias, qf, kf, vf, tile * TN, tile >= n_full, lim, lane);
+            attend_tile_biased<F16, NKB, hoist>(st, bias, qf, kf, vf, tile * TN, tile >= n_full, lim, lane);
         else
             attend_tile<F16, NKB, EXT, hoist>(st, qf, kf, vf, tile * TN,
                                               tile >= n_full || (EXT && tile < first_full), lim, c2, lane,
