@@ -472,125 +472,6 @@ __device__ __forceinline__ void attend_tile(RowState &st, const u32x4 (&qf)[8], 
     tile_pv<F16, NKB>(st, pf, vfrag);
 }
 
-// fp16, score accumulators started from the row's reference: the query
-// fragments were scaled by c2 (the score scale in log2 units) when loaded,
-// and every score chain starts from bias = -m (m the row's reference max, 0
-// while the row has none) instead of 0, so the MFMAs leave s * c2 - m and a
-// weight is a single exponential.  When some row's max grows past the lazy
-// rescale threshold (rare after the first tiles), the tile's scores of those
-// rows are shifted by the growth and their bias is rewritten; otherwise the
-// same steps as tile_softmax.
-template <bool F16, int NKB>
-__device__ __forceinline__ void tile_softmax_biased(RowState &st, f32x16 &bias, f32x16 (&sacc)[NKB],
-                                                    u32x4 (&pf)[2 * NKB], int key0, bool masked, int lim,
-                                                    int lane) {
-    const int hl = lane >> 5;
-    if (masked) {
-        const int j0 = key0 + 8 * hl;
-#pragma unroll
-        for (int b = 0; b < NKB; ++b)
-#pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                const int j = j0 + 32 * b + 16 * (q >> 3) + (q & 7);
-                if (j >= lim)
-                    sacc[b][q] = neg_inf();
-            }
-    }
-    float mx = neg_inf();
-#pragma unroll
-    for (int b = 0; b < NKB; ++b)
-#pragma unroll
-        for (int q = 0; q < 16; ++q)
-            mx = fmaxf(mx, sacc[b][q]);
-    mx = xhalf_max(mx);                         // (tile max of s * c2) - m_use
-    // a row without a reference takes its first finite max; later the
-    // reference moves only when the tile's max exceeds it by kRescaleLog2
-    const bool grow = (st.m == neg_inf()) ? (mx != neg_inf()) : (mx > kRescaleLog2);
-    if (__ballot(grow) != 0) {
-        const float m_use = (st.m == neg_inf()) ? 0.0f : st.m;
-        const float tmax = mx + m_use;
-        const float alpha = grow ? __builtin_amdgcn_exp2f(st.m - tmax) : 1.0f;   // 0 if m was -inf
-        const float shift = grow ? mx : 0.0f;
-        st.m = grow ? tmax : st.m;
-        st.l *= alpha;
-#pragma unroll
-        for (int x = 0; x < 4; ++x)
-            st.o[x] *= alpha;
-#pragma unroll
-        for (int b = 0; b < NKB; ++b)
-#pragma unroll
-            for (int q = 0; q < 16; ++q)
-                sacc[b][q] -= shift;
-        const float nb = (st.m == neg_inf()) ? 0.0f : -st.m;
-#pragma unroll
-        for (int q = 0; q < 16; ++q)
-            bias[q] = nb;
-    }
-    // weights, the 16-bit B operand and the row sum, as in tile_softmax
-    float rs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int b = 0; b < NKB; ++b)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            const float p = __builtin_amdgcn_exp2f(sacc[b][q]);
-            sacc[b][q] = p;
-            if constexpr (!F16)
-                rs[q & 3] += p;
-        }
-#pragma unroll
-    for (int b = 0; b < NKB; ++b)
-#pragma unroll
-        for (int hsel = 0; hsel < 2; ++hsel) {
-            const int q0 = 8 * hsel;
-            if constexpr (F16) {
-                const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
-                f16x2 h[4];
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    h[w] = f16x2{(_Float16)sacc[b][q0 + 2 * w], (_Float16)sacc[b][q0 + 2 * w + 1]};
-                    rs[w] = __builtin_amdgcn_fdot2(h[w], ones, rs[w], false);
-                }
-                pf[2 * b + hsel] = u32x4{__builtin_bit_cast(uint32_t, h[0]), __builtin_bit_cast(uint32_t, h[1]),
-                                         __builtin_bit_cast(uint32_t, h[2]), __builtin_bit_cast(uint32_t, h[3])};
-            } else {
-                pf[2 * b + hsel] = u32x4{pack2<F16>(sacc[b][q0 + 0], sacc[b][q0 + 1]),
-                                         pack2<F16>(sacc[b][q0 + 2], sacc[b][q0 + 3]),
-                                         pack2<F16>(sacc[b][q0 + 4], sacc[b][q0 + 5]),
-                                         pack2<F16>(sacc[b][q0 + 6], sacc[b][q0 + 7])};
-            }
-        }
-    st.l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
-}
-
-// attend_tile with pre-scaled queries and biased score chains
-// (tile_softmax_biased).  HOIST: K fragments read ahead of the chain, as in
-// tile_scores.
-template <bool F16, int NKB, bool HOIST, class KF, class VF>
-__device__ __forceinline__ void attend_tile_biased(RowState &st, f32x16 &bias, const u32x4 (&qf)[8], KF kfrag,
-                                                   VF vfrag, int key0, bool masked, int lim, int lane) {
-    f32x16 sacc[NKB];
-    u32x4 pf[2 * NKB];
-    u32x4 kall[HOIST ? 8 : 1][HOIST ? NKB : 1];
-    if constexpr (HOIST) {
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-            for (int b = 0; b < NKB; ++b)
-                kall[ks][b] = kfrag(b, ks);
-    }
-    __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-        for (int b = 0; b < NKB; ++b) {
-            const u32x4 kf = HOIST ? kall[HOIST ? ks : 0][HOIST ? b : 0] : kfrag(b, ks);
-            sacc[b] = mfma32<F16>(kf, qf[ks], ks == 0 ? bias : sacc[b]);
-        }
-    __builtin_amdgcn_s_setprio(0);
-    tile_softmax_biased<F16, NKB>(st, bias, sacc, pf, key0, masked, lim, lane);
-    tile_pv<F16, NKB>(st, pf, vfrag);
-}
-
 // V^T fragment from a row-major [keys][128] LDS V tile with the swz_v layout,
 // by two transposing reads.  Lane j of 16-lane group g = lane/16 points at key
 // 16kk + 8(g>>1) + 4t + j/4 (t = 0, 1), d 32x + 16(g&1) + 4(j%4) .. +3, and
@@ -841,32 +722,6 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, int bx, int spli
     const bool wave_on = wv * 32 < (tq1 - tq0) * G;       // uniform over the wave
     u32x4 qf[8];
     load_q(a, qf, row_ok, tok, head, lane);
-    // fp16 queries without a window or ALiBi: the score chains start from
-    // the row's reference (tile_softmax_biased), with the query rows scaled
-    // by the score scale (and an fp8 cache's K scale) once here, each element
-    // rounded to fp16 once more.  Not for bf16: that rounding (2^-9) moves
-    // the log-sum-exp by about 1e-3.
-    constexpr bool biased = F16 && !EXT;
-    f32x16 bias = f32x16{};
-    if constexpr (biased) {
-        const float cq = a.scale_log2 * (FP8KV ? *a.k_scale : 1.0f);
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            if constexpr (F16) {
-                f16x8 h = __builtin_bit_cast(f16x8, qf[ks]);
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    h[e] = (_Float16)((float)h[e] * cq);
-                qf[ks] = __builtin_bit_cast(u32x4, h);
-            } else {
-                bf16x8 h = __builtin_bit_cast(bf16x8, qf[ks]);
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    h[e] = (__bf16)((float)h[e] * cq);
-                qf[ks] = __builtin_bit_cast(u32x4, h);
-            }
-        }
-    }
 
     // ---------------------------------------------------------------- paging
     const int32_t *btrow = a.block_table + (int64_t)s * a.bt_stride;
@@ -890,12 +745,9 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, int bx, int spli
         // cache, one key group, no window or ALiBi (bf16 mixed batches and
         // the ALiBi path measured about 1 % slower with it)
         constexpr bool hoist = F16 && !FP8KV && KG == 1 && !EXT;
-        if constexpr (biased)
-            attend_tile_biased<F16, NKB, hoist>(st, bias, qf, kf, vf, tile * TN, tile >= n_full, lim, lane);
-        else
-            attend_tile<F16, NKB, EXT, hoist>(st, qf, kf, vf, tile * TN,
-                                              tile >= n_full || (EXT && tile < first_full), lim, c2, lane,
-                                              ext, alibi);
+        attend_tile<F16, NKB, EXT, hoist>(st, qf, kf, vf, tile * TN,
+                                          tile >= n_full || (EXT && tile < first_full), lim, c2, lane,
+                                          ext, alibi);
     };
 
     if constexpr (!FP8KV) {

@@ -55,6 +55,27 @@ def test_decode_kernel_only_when_short_sequences_possible(q_short, decode_kernel
     H.compare(wl, out, lse, what=f"decode rule {q_short}")
 
 
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_large_softmax_scale(dtype):
+    # softmax scale 1.3 (the backward benchmark's) with N(0,1) inputs and
+    # d = 128: scores reach about 100 in log2 units, so a rounding applied to
+    # a score's inputs before its exponential (a query pre-scaled by the score
+    # scale and rounded to fp16, say) shows in the log-sum-exp at about that
+    # magnitude times its relative size; every row against the oracle
+    # (log-sum-exp within the usual 1e-3).  At this scale a row's weights
+    # are so peaked that its output is nearly one value row (|v| up to about
+    # 5 here), so the output bound is the arithmetic's own: each weight is
+    # rounded to the q dtype (relative u: 2^-8 bf16, 2^-11 fp16) and the
+    # output once more, |err| <= 2u max|v|, or the usual 2e-2 if larger.
+    wl = wk.make_paged("large_scale", 5300 + (dtype == "bf16"), [1024, 700], [1024, 900], 8, 8,
+                       block_size=16, dtype=dtype, causal=True, softmax_scale=1.3)
+    H.say(f"softmax scale 1.3 {dtype}")
+    out, lse = H.run(wl)
+    u = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -11
+    vmax = float(wl.v_cache.float().abs().max())
+    H.compare(wl, out, lse, tol=max(2e-2, 2 * u * vmax), what=f"scale 1.3 {dtype}")
+
+
 @pytest.mark.parametrize("causal", [True, False])
 def test_config2_dense_full_size_sampled(causal):
     wl = wk.config2(causal=causal)
