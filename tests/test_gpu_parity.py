@@ -55,25 +55,40 @@ def test_decode_kernel_only_when_short_sequences_possible(q_short, decode_kernel
     H.compare(wl, out, lse, what=f"decode rule {q_short}")
 
 
-@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
-def test_large_softmax_scale(dtype):
+SCALE_CASES = [
+    # (dtype, kv_dtype, q_lens, kv_lens, (Hq, Hkv), num_splits, softmax_scale)
+    ("fp16", None, [1024, 700], [1024, 900], (8, 8), 1, 1.3),
+    ("bf16", None, [1024, 700], [1024, 900], (8, 8), 1, 1.3),
+    ("bf16", None, [1, 3, 40, 200], [2000, 1500, 900, 700], (32, 4), 1, 1.3),   # decode rows too
+    ("bf16", None, [1, 3, 40, 200], [2000, 1500, 900, 700], (32, 4), 4, 1.3),   # split + combine
+    ("fp16", "fp8_e4m3fn", [1, 64, 300], [1200, 800, 600], (8, 2), 1, 1.3),
+    ("bf16", None, [1, 128, 500], [3000, 900, 500], (8, 2), 1, 0.02),           # nearly flat weights
+]
+
+
+@pytest.mark.parametrize("case", range(len(SCALE_CASES)))
+def test_softmax_scale_extremes(case):
     # softmax scale 1.3 (the backward benchmark's) with N(0,1) inputs and
     # d = 128: scores reach about 100 in log2 units, so a rounding applied to
     # a score's inputs before its exponential (a query pre-scaled by the score
     # scale and rounded to fp16, say) shows in the log-sum-exp at about that
-    # magnitude times its relative size; every row against the oracle
-    # (log-sum-exp within the usual 1e-3).  At this scale a row's weights
-    # are so peaked that its output is nearly one value row (|v| up to about
-    # 5 here), so the output bound is the arithmetic's own: each weight is
-    # rounded to the q dtype (relative u: 2^-8 bf16, 2^-11 fp16) and the
-    # output once more, |err| <= 2u max|v|, or the usual 2e-2 if larger.
-    wl = wk.make_paged("large_scale", 5300 + (dtype == "bf16"), [1024, 700], [1024, 900], 8, 8,
-                       block_size=16, dtype=dtype, causal=True, softmax_scale=1.3)
-    H.say(f"softmax scale 1.3 {dtype}")
-    out, lse = H.run(wl)
+    # magnitude times its relative size; and scale 0.02, where every key
+    # weighs about the same.  Prefill and decode rows, unsplit and split,
+    # 16-bit and e4m3 caches, every row against the oracle (log-sum-exp
+    # within the usual 1e-3).  At scale 1.3 a row's weights are so peaked
+    # that its output is nearly one value row (|v| up to about 5 here), so
+    # the output bound is the arithmetic's own: each weight is rounded to the
+    # q dtype (relative u: 2^-8 bf16, 2^-11 fp16) and the output once more,
+    # |err| <= 2u max|v|, or the usual bar if larger.
+    dtype, kv_dtype, q_lens, kv_lens, heads, splits, scale = SCALE_CASES[case]
+    wl = wk.make_paged("scale_extremes", 5300 + case, q_lens, kv_lens, heads[0], heads[1],
+                       block_size=16, dtype=dtype, kv_dtype=kv_dtype, causal=True, softmax_scale=scale)
+    H.say(f"softmax scale {scale} {dtype} kv={kv_dtype} q={q_lens} splits={splits}")
+    out, lse = H.run(wl, num_splits=splits)
     u = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -11
-    vmax = float(wl.v_cache.float().abs().max())
-    H.compare(wl, out, lse, tol=max(2e-2, 2 * u * vmax), what=f"scale 1.3 {dtype}")
+    vmax = float(wl.v_cache.float().abs().max()) * (1.0 if wl.v_scale is None else wl.v_scale)
+    base = H.TOL["fp8_e4m3fn"] if kv_dtype else H.TOL[dtype]
+    H.compare(wl, out, lse, tol=max(base, 2 * u * vmax), what=f"scale case {case}")
 
 
 @pytest.mark.parametrize("causal", [True, False])
