@@ -279,6 +279,20 @@ def test_plan_mixed_splits_decode_rows_only(lib):
     assert st == 0 and info.kernels == 3 and info.grid_y == 4 and info.num_waves == 8
 
 
+@pytest.mark.parametrize("extra,decode", [(5, False), (4, True), (0, True)])
+def test_plan_decode_kernel_rule_gqa8(lib, extra, decode):
+    # G = 8 (64 q heads, 8 kv heads): a sequence is a decode sequence when
+    # q_len * 8 <= 32, i.e. q_len <= 4.  Three sequences, max_seqlen_q 100,
+    # T = 200 + extra: the shortest has at least `extra` tokens, so the
+    # decode kernel runs (bit 1, S x Hkv decode workgroups) only when extra <= 4
+    p = base_params(num_seqs=3, num_tokens=200 + extra, num_q_heads=64, num_kv_heads=8,
+                    max_seqlen_q=100, max_seqlen_k=2048,
+                    q_stride_token=64 * 128, o_stride_token=64 * 128)
+    st, info = plan_status(lib, p)
+    assert st == 0 and info.kernels & 1 and bool(info.kernels & 2) == decode
+    assert info.decode_grid_x == (3 * 8 if decode else 0) and info.num_splits == 1
+
+
 def test_plan_no_decode_split_without_decode_rows(lib):
     # dense 4 x 4096 (G = 1): every sequence has 4096 tokens, none can be a
     # decode sequence, so automatic choice leaves the launch unsplit
