@@ -10,9 +10,17 @@
 
 namespace ua {
 
-hipError_t launch_attention(const AttnArgs &a, bool, bool, bool, bool, bool wide, dim3 grid,
+hipError_t launch_attention(const AttnArgs &a, bool, bool, bool, bool split, bool wide, bool mix, dim3 grid,
                             hipStream_t) {
-    if (grid.x == 0 || grid.y == 0 || (wide && a.num_splits < 2))
+    if (grid.x == 0 || grid.y == 0 || (wide && a.num_splits < 2) || (wide && !split))
+        std::abort();
+    // a launch that splits only the decode rows: unsplit prefill workgroups,
+    // a one-dimensional grid holding every decode block
+    if (mix && (split || a.num_splits < 2 || grid.y != 1 || a.mix_region < a.mix_dblocks ||
+                (int64_t)grid.x < 8LL * a.mix_dblocks))
+        std::abort();
+    // persistent form: at most one workgroup per item
+    if (a.persist_items > 0 && (int64_t)grid.x * grid.y > a.persist_items)
         std::abort();
     return hipSuccess;
 }
@@ -21,6 +29,15 @@ hipError_t launch_combine(const float *o_part, const float *lse_part, int32_t nu
                           int32_t, void *out, bool, int64_t, int64_t, float *, const int32_t *,
                           hipStream_t) {
     if (!o_part || !lse_part || !out || num_splits < 1 || rows < 0)
+        std::abort();
+    return hipSuccess;
+}
+
+hipError_t launch_combine_decode(const float *o_part, const float *lse_part, int32_t num_splits, int64_t rows,
+                                 int32_t, int32_t num_kv_heads, int32_t num_seqs, const int32_t *cu_seqlens_q,
+                                 void *out, bool, int64_t, int64_t, float *, hipStream_t) {
+    if (!o_part || !lse_part || !out || !cu_seqlens_q || num_splits < 2 || rows < 0 || num_kv_heads <= 0 ||
+        num_seqs < 0)
         std::abort();
     return hipSuccess;
 }
