@@ -91,6 +91,17 @@ def test_softmax_scale_extremes(case):
     H.compare(wl, out, lse, tol=max(base, 2 * u * vmax), what=f"scale case {case}")
 
 
+@pytest.mark.parametrize("i", range(60))
+def test_random_feature_sweep(i):
+    # seeded random batches across the forward's features (workloads.
+    # random_feature_case), every row against the oracle
+    wl, splits = wk.random_feature_case(i)
+    H.say(f"sweep {i}: q={wl.q_lens.tolist()} kv={wl.kv_lens.tolist()} heads={wl.num_q_heads}/"
+          f"{wl.num_kv_heads} causal={wl.causal} splits={splits}")
+    out, lse = H.run(wl, num_splits=splits)
+    H.compare(wl, out, lse, what=f"sweep {i}")
+
+
 @pytest.mark.parametrize("causal", [True, False])
 def test_config2_dense_full_size_sampled(causal):
     wl = wk.config2(causal=causal)

@@ -464,6 +464,39 @@ def random_small(seed: int, *, max_seqs: int = 4, max_kv: int = 70, heads=(4, 2)
                       softmax_scale=float(rng.uniform(0.02, 0.2)))
 
 
+def random_feature_case(i: int) -> tuple:
+    """Case i of a seeded sweep across the forward's features: G 1..16, 1-6
+    sequences mixing decode-like (q 0..4), short and long prefill rows, kv up
+    to q + 1000, bf16/fp16 queries, 16-bit or e4m3 caches, pages of 16-128,
+    causal or full, default or random scales, split counts 1/auto/2..8 and
+    decode-row splits, and now and then a local window and / or ALiBi.
+    Returns (workload, num_splits)."""
+    import random
+    rng = random.Random(31000 + int(i))
+    G = rng.choice([1, 2, 3, 4, 8, 16]); hkv = rng.choice([1, 2, 4]); hq = G * hkv
+    ql, kl = [], []
+    for _ in range(rng.randint(1, 6)):
+        r = rng.random()
+        q = rng.randint(0, 4) if r < 0.3 else (rng.randint(5, 70) if r < 0.65 else rng.randint(70, 200))
+        ql.append(q)
+        kl.append(max(1, q + rng.randint(0, 1000)))
+    dtype = rng.choice(["bf16", "fp16"])
+    kvd = rng.choice([None, None, "fp8_e4m3fn"])
+    bs = rng.choice([16, 32, 64, 128])
+    causal = rng.random() < 0.7
+    scale = None if rng.random() < 0.5 else rng.uniform(0.02, 0.3)
+    splits = rng.choice([1, 1, 0, 2, 3, 4, 8, -2, -4])
+    wl = make_paged(f"sweep{i}", 31000 + int(i), ql, kl, hq, hkv, block_size=bs, dtype=dtype, kv_dtype=kvd,
+                    causal=causal, softmax_scale=scale)
+    if rng.random() < 0.25:
+        left = rng.choice([-1, rng.randint(0, 300)])
+        right = rng.choice([-1, rng.randint(0, 50)]) if not causal else -1
+        slopes = alibi_slopes(hq) if rng.random() < 0.5 else None
+        if left >= 0 or right >= 0 or slopes is not None:
+            wl = with_mask(wl, left, right, slopes)
+    return wl, splits
+
+
 # --------------------------------------------------------------------------- backward
 
 def backward_case(seed: int, q_lens: Sequence[int], k_lens: Sequence[int], num_q_heads: int,
