@@ -84,6 +84,21 @@ def test_backward_parity(case_def):
     check_close(got, ref, U[dt], "vs oracle", name)
 
 
+@pytest.mark.parametrize("i", range(40))
+def test_backward_random_sweep(i):
+    # seeded random batches across the backward's features
+    # (workloads.backward_feature_case), every entry against the oracle
+    case, causal = wk.backward_feature_case(i)
+    dt = "fp16" if case["q"].dtype == torch.float16 else "bf16"
+    ref = oracle_case(case, causal)
+    out = torch.from_numpy(ref["out"]).to(case["q"].dtype)
+    lse = torch.from_numpy(ref["lse"]).to(torch.float32)
+    say(f"backward sweep {i}: q_lens={np.diff(case['cu_seqlens_q'].numpy()).tolist()} "
+        f"k_lens={np.diff(case['cu_seqlens_k'].numpy()).tolist()} causal={causal} {dt}")
+    got = hip_backward(case, causal, out, lse)
+    check_close(got, ref, U[dt], "vs oracle", f"sweep {i}")
+
+
 def _paged_view(case):
     """The dense k, v as a paged cache with 16-key pages (every cu_seqlens_k[s]
     a multiple of 16) and the tables that map it back."""

@@ -530,6 +530,26 @@ def backward_bench(batch: int = 4, heads: int = 32, seq: int = 4096) -> dict:
     return backward_case(8, [seq] * batch, [seq] * batch, heads, heads, "fp16", softmax_scale=1.3)
 
 
+def backward_feature_case(i: int) -> tuple:
+    """Case i of a seeded sweep across the backward's features: G 1..8,
+    1-4 sequences with empty, single-row, short and long query runs, keys
+    at least the queries (causal) or anything from none to 450 (full),
+    bf16/fp16, default or random scales.  Returns (case, causal)."""
+    import random
+    rng = random.Random(41000 + int(i))
+    G = rng.choice([1, 2, 3, 4, 8]); hkv = rng.choice([1, 2])
+    causal = rng.random() < 0.6
+    ql, kl = [], []
+    for _ in range(rng.randint(1, 4)):
+        q = rng.choice([0, 1, rng.randint(2, 40), rng.randint(40, 150)])
+        k = q + rng.randint(0, 300) if causal else rng.choice([0, rng.randint(1, 40), rng.randint(40, 450)])
+        ql.append(q)
+        kl.append(k)
+    dt = rng.choice(["bf16", "fp16"])
+    scale = None if rng.random() < 0.5 else rng.uniform(0.05, 0.6)
+    return backward_case(41000 + int(i), ql, kl, G * hkv, hkv, dt, softmax_scale=scale), causal
+
+
 def fp8_weight_pin_case(q_len: int = 40) -> Workload:
     """A designed batch for the e4m3 rounding of the softmax weights in the
     fp8-compute mode: one sequence of q_len queries (one head, so every row is
