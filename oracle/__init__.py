@@ -118,7 +118,7 @@ def attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     """
     lib = lib or load()
     for t in (q, k_cache, v_cache):
-        if t.stride(-1) != 1:
+        if t.numel() and t.stride(-1) != 1:          # an empty tensor has no layout to check
             raise ValueError("unit stride along head_size required")
     if k_cache.stride() != v_cache.stride() or k_cache.dtype != v_cache.dtype:
         raise ValueError("k_cache and v_cache must share dtype and strides")
