@@ -294,7 +294,7 @@ def test_edge_shapes(q_lens, kv_lens, heads, bs, causal):
     H.compare(wl, out, lse, what="edge")
 
 
-@pytest.mark.parametrize("bs", [128, 256, 1024])
+@pytest.mark.parametrize("bs", [128, 256, 1024, 4096])
 @pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3fn"])
 @pytest.mark.parametrize("causal,splits", [(True, 1), (True, 3), (False, 1)])
 def test_large_pages(bs, kv_dtype, causal, splits):
