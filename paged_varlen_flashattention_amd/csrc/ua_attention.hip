@@ -42,8 +42,10 @@
 // Paged KV gather: key j of sequence s is slot j % bs of physical block
 // block_table[s][j / bs] (page "vLLM Triton unified attention notes", section
 // kernel_unified_attention_2d: four element strides).  fp8 e4m3fn codes are
-// widened to the q dtype on the way into LDS or registers (exact); k_scale is
-// folded into the score scale and v_scale into the epilogue.
+// widened to the q dtype (exact): the prefill body keeps a tile's codes in LDS
+// and widens each operand fragment as it reads it, the decode body widens on
+// the way into LDS; k_scale is folded into the score scale and v_scale into
+// the epilogue.
 //
 // Split-KV (page "flashatten takeaways EP2 工程", section "源代码接口"; page
 // "Fused Attention", section FlashDecoding): each split owns a contiguous run
@@ -461,6 +463,30 @@ __device__ __forceinline__ void tile_pv(RowState &st, const u32x4 (&pf)[2 * NKB]
             st.o[x] = mfma32<F16>(vfrag(kk, x), pf[kk], st.o[x]);
 }
 
+// S^T of the tile from fp8 K codes (the PAIRED d order of load_q): kpair(b,
+// j, f0, f1) widens one 16-byte read of block b's key row into the operands of
+// k-steps 2j and 2j+1.  Per block the k-steps still run in ascending order.
+template <bool F16, int NKB, class KP>
+__device__ __forceinline__ void tile_scores_paired(f32x16 (&sacc)[NKB], const u32x4 (&qf)[8], KP kpair) {
+#pragma unroll
+    for (int b = 0; b < NKB; ++b)
+        sacc[b] = f32x16{};
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        u32x4 f[NKB][2];
+#pragma unroll
+        for (int b = 0; b < NKB; ++b)
+            kpair(b, j, f[b][0], f[b][1]);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int b = 0; b < NKB; ++b)
+                sacc[b] = mfma32<F16>(f[b][h], qf[2 * j + h], sacc[b]);
+    }
+    __builtin_amdgcn_s_setprio(0);
+}
+
 template <bool F16, int NKB, bool EXT = false, bool HOIST = false, class KF, class VF>
 __device__ __forceinline__ void attend_tile(RowState &st, const u32x4 (&qf)[8], KF kfrag, VF vfrag,
                                             int key0, bool masked, int lim, float c2, int lane,
@@ -468,6 +494,17 @@ __device__ __forceinline__ void attend_tile(RowState &st, const u32x4 (&qf)[8], 
     f32x16 sacc[NKB];
     u32x4 pf[2 * NKB];
     tile_scores<F16, NKB, HOIST>(sacc, qf, kfrag);
+    tile_softmax<F16, NKB, EXT>(st, sacc, pf, key0, masked, lim, c2, lane, ext, alibi);
+    tile_pv<F16, NKB>(st, pf, vfrag);
+}
+
+template <bool F16, int NKB, bool EXT = false, class KP, class VF>
+__device__ __forceinline__ void attend_tile_paired(RowState &st, const u32x4 (&qf)[8], KP kpair, VF vfrag,
+                                                   int key0, bool masked, int lim, float c2, int lane,
+                                                   RowExt ext = RowExt{0, 0, 0.0f}, bool alibi = false) {
+    f32x16 sacc[NKB];
+    u32x4 pf[2 * NKB];
+    tile_scores_paired<F16, NKB>(sacc, qf, kpair);
     tile_softmax<F16, NKB, EXT>(st, sacc, pf, key0, masked, lim, c2, lane, ext, alibi);
     tile_pv<F16, NKB>(st, pf, vfrag);
 }
@@ -553,14 +590,21 @@ __device__ __forceinline__ void poison_row(const AttnArgs &a, int64_t tok, int h
 }
 
 // Q fragments of row (tok, head): B operand of S^T = K Q^T, k-step ks covers
-// d 16ks .. 16ks+15 (8 per lane half).  Zero for rows that do not exist.
+// d 16ks .. 16ks+15 (8 per lane half).  PAIRED (the fp8-cache prefill path):
+// k-steps 2j and 2j+1 of lane half h cover d 32j + 16h .. 32j + 16h + 15, so
+// one 16-byte read of a key row's codes gives a lane both steps' K operands.
+// Zero for rows that do not exist.
+template <bool PAIRED = false>
 __device__ __forceinline__ void load_q(const AttnArgs &a, u32x4 (&qf)[8], bool row_ok, int64_t tok,
                                        int head, int lane) {
     if (row_ok) {
         const uint8_t *qp = (const uint8_t *)a.q + (tok * a.q_st_tok + (int64_t)head * a.q_st_head) * 2;
+        const int hl = lane >> 5;
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks)
-            qf[ks] = *(const u32x4 *)(qp + (16 * ks + 8 * (lane >> 5)) * 2);
+        for (int ks = 0; ks < 8; ++ks) {
+            const int d0 = PAIRED ? 32 * (ks >> 1) + 16 * hl + 8 * (ks & 1) : 16 * ks + 8 * hl;
+            qf[ks] = *(const u32x4 *)(qp + d0 * 2);
+        }
     } else {
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks)
@@ -721,7 +765,7 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, int bx, int spli
     const int wv = __builtin_amdgcn_readfirstlane(wave);
     const bool wave_on = wv * 32 < (tq1 - tq0) * G;       // uniform over the wave
     u32x4 qf[8];
-    load_q(a, qf, row_ok, tok, head, lane);
+    load_q<FP8KV>(a, qf, row_ok, tok, head, lane);
 
     // ---------------------------------------------------------------- paging
     const int32_t *btrow = a.block_table + (int64_t)s * a.bt_stride;
@@ -734,46 +778,91 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, int bx, int spli
     const float c2 = a.scale_log2 * (FP8KV ? *a.k_scale : 1.0f);   // score -> log2 units
     RowState st;
     init_rows(st);
+    // fp8 caches: the tile holds codes (128-byte key rows, 16-byte chunks) and
+    // the operands are widened to the q dtype as they are read.  K chunk c of
+    // key k sits at position c ^ ((k >> 1) & 7): the 16 lanes of a 16-byte
+    // read take 16 different keys (both parities of 8 key pairs) and hit 16
+    // distinct 16-byte bank groups.  V chunk c of key k sits at
+    // c ^ 2((k >> 1) & 3): the 32 lanes of an 8-bit transposing read take 8
+    // consecutive keys x chunks 2x, 2x+1 and hit 32 distinct 8-byte groups.
     auto compute = [&](int tile, const uint8_t *sK, const uint8_t *sV) {
-        const uint8_t *krow = sK + swap23(lc) * 256;
-        auto kf = [&](int b, int ks) {
-            return *(const u32x4 *)(krow + 32 * b * 256 + (((2 * ks + hl) ^ (lane & 15)) << 4));
-        };
-        auto vf = [&](int kk, int x) { return vfrag_lds(sV, kk, x, lane); };
-        // the K fragments are read ahead of the score chain where that
-        // measured faster and the register file has room: fp16, 16-bit
-        // cache, one key group, no window or ALiBi (bf16 mixed batches and
-        // the ALiBi path measured about 1 % slower with it)
-        constexpr bool hoist = F16 && !FP8KV && KG == 1 && !EXT;
-        attend_tile<F16, NKB, EXT, hoist>(st, qf, kf, vf, tile * TN,
-                                          tile >= n_full || (EXT && tile < first_full), lim, c2, lane,
-                                          ext, alibi);
+        if constexpr (FP8KV) {
+            const int k8swz = (swap23(lc) >> 1) & 7;            // K position XOR of this lane's rows
+            const int te = (lane & 15) >> 1, tp = lane & 1;     // transposing-read source row, half
+            const int v8swz = 2 * ((te >> 1) & 3);              // V position XOR of key 8h + te
+            const int vchunk = (lane >> 4) & 1;                 // chunk 2x + vchunk
+            // block b, k-steps 2j, 2j+1: key 32b + swap23(lc), d 32j + 16hl + 0..15
+            const uint8_t *krow = sK + swap23(lc) * 128;
+            auto kp = [&](int b, int j, u32x4 &f0, u32x4 &f1) {
+                const u32x4 w = *(const u32x4 *)(krow + 32 * b * 128 + (((2 * j + hl) ^ k8swz) << 4));
+                f0 = widen_fp8<F16>(u32x2{w[0], w[1]});
+                f1 = widen_fp8<F16>(u32x2{w[2], w[3]});
+            };
+            // V^T operand of 16-key step kk, d block x: lane (h, lc) receives
+            // keys 16kk + 8h + 0..7 at d 32x + lc (byte e = key 16kk + 8h + e)
+            const uint8_t *vrow = sV + (8 * hl + te) * 128 + 8 * tp;
+            auto vf = [&](int kk, int x) {
+                const uint8_t *src = vrow + kk * 16 * 128 + ((((2 * x) ^ v8swz) + vchunk) << 4);
+                const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                    (__attribute__((address_space(3))) i32x2 *)(src));
+                return widen_fp8<F16>(u32x2{(uint32_t)w[0], (uint32_t)w[1]});
+            };
+            attend_tile_paired<F16, NKB, EXT>(st, qf, kp, vf, tile * TN,
+                                              tile >= n_full || (EXT && tile < first_full), lim, c2,
+                                              lane, ext, alibi);
+        } else {
+            const uint8_t *krow = sK + swap23(lc) * 256;
+            auto kf = [&](int b, int ks) {
+                return *(const u32x4 *)(krow + 32 * b * 256 + (((2 * ks + hl) ^ (lane & 15)) << 4));
+            };
+            auto vf = [&](int kk, int x) { return vfrag_lds(sV, kk, x, lane); };
+            // the K fragments are read ahead of the score chain where that
+            // measured faster and the register file has room: fp16, one key
+            // group, no window or ALiBi (bf16 mixed batches and the ALiBi
+            // path measured about 1 % slower with it)
+            constexpr bool hoist = F16 && KG == 1 && !EXT;
+            attend_tile<F16, NKB, EXT, hoist>(st, qf, kf, vf, tile * TN,
+                                              tile >= n_full || (EXT && tile < first_full), lim, c2,
+                                              lane, ext, alibi);
+        }
     };
 
-    if constexpr (!FP8KV) {
-        // 16-bit caches: K/V go straight from HBM into LDS (global_load_lds,
-        // 16 bytes per lane), no register staging.  Wave w fills keys
-        // 16w .. 16w+15 of the tile (one page: a page holds >= 16 keys) with
-        // four 4-key instructions per tensor; lane l of an instruction lands
-        // at LDS byte 16*l of those 4 rows, so it fetches the d chunk whose
-        // swizzled position that is.  The DMA of tile + 1 runs under the
-        // compute of tile; one barrier per tile.  The page id is a scalar load
-        // fetched a tile ahead.
-        // per-lane global offsets of the four 4-key instructions per tensor
-        // (the row group included, so all four share the page's scalar
-        // base); m0 of each instruction is the wave's first row in the
-        // group's LDS area plus a compile-time offset
-        const int lrow = lane >> 4;                           // row within a 4-key group
-        uint32_t koff[4], voff[4];
+    {
+        // K/V go straight from HBM into LDS (global_load_lds, 16 bytes per
+        // lane), no register staging; fp8 caches stay codes in LDS (widened
+        // as the operands are read).  Wave w fills keys 16w .. 16w+15 of the
+        // tile (one page: a page holds >= 16 keys): 16-bit rows with four
+        // 4-key instructions per tensor, fp8 rows with two 8-key
+        // instructions.  Lane l of an instruction lands at LDS byte 16*l of
+        // its rows, so it fetches the chunk whose swizzled position that is.
+        // The DMA of tile + 1 runs under the compute of tile; one barrier per
+        // tile.  The page id is a scalar load fetched a tile ahead.
+        constexpr int RB = 128 * KVB;                     // bytes of a key row in LDS
+        constexpr int NI = FP8KV ? 2 : 4;                 // instructions per tensor and tile
+        constexpr int RPI = 16 / NI;                      // key rows per instruction
+        constexpr int CPR = RB / 16;                      // 16-byte chunks per row
+        // per-lane global offsets of the instructions (the row group
+        // included, so all share the page's scalar base); m0 of each
+        // instruction is the wave's first row in the group's LDS area plus a
+        // compile-time offset
+        const int lrow = FP8KV ? lane >> 3 : lane >> 4;  // row within an instruction's group
+        const int pc = lane & (CPR - 1);                  // chunk position within the row
+        uint32_t koff[NI], voff[NI];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t rofs = (uint32_t)((4 * i + lrow) * a.kv_st_slot * KVB);
-            koff[i] = rofs + (uint32_t)(((lane & 15) ^ swz_k(4 * i + lrow)) << 4);
-            voff[i] = rofs + (uint32_t)(((lane & 15) ^ swz_v(lrow)) << 4);
+        for (int i = 0; i < NI; ++i) {
+            const uint32_t rofs = (uint32_t)((RPI * i + lrow) * a.kv_st_slot * KVB);
+            if constexpr (FP8KV) {
+                const int kl = RPI * i + lrow;            // key within the wave's 16 (same bits 1..3)
+                koff[i] = rofs + (uint32_t)((pc ^ ((kl >> 1) & 7)) << 4);
+                voff[i] = rofs + (uint32_t)((pc ^ (2 * ((kl >> 1) & 3))) << 4);
+            } else {
+                koff[i] = rofs + (uint32_t)((pc ^ swz_k(RPI * i + lrow)) << 4);
+                voff[i] = rofs + (uint32_t)((pc ^ swz_v(lrow)) << 4);
+            }
         }
-        const int wrow = 16 * wv;                             // this wave's first key in the tile
+        const int wrow = 16 * wv;                         // this wave's first key in the tile
         const uint32_t lds_row0 = (uint32_t)reinterpret_cast<uintptr_t>(
-            (__attribute__((address_space(3))) uint8_t *)(sK0)) + (uint32_t)(wrow * 256);
+            (__attribute__((address_space(3))) uint8_t *)(sK0)) + (uint32_t)(wrow * RB);
         int32_t blk = 0;
         auto fetch_id = [&](int tile) {
             blk = sload(btrow + min((tile * TN + wrow) >> lbs, last_page));
@@ -785,25 +874,28 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, int bx, int spli
             const int64_t pofs =
                 ((int64_t)blk * a.kv_st_blk + (int64_t)(j & bs_mask) * a.kv_st_slot) * KVB;
             const uint8_t *gk = kbase + pofs, *gv = vbase + pofs;
-            lds_dma16_at<KOFS + 0 * 256>(gk, koff[0], lds_row0);
-            lds_dma16_at<VOFS + 0 * 256>(gv, voff[0], lds_row0);
-            lds_dma16_at<KOFS + 4 * 256>(gk, koff[1], lds_row0);
-            lds_dma16_at<VOFS + 4 * 256>(gv, voff[1], lds_row0);
-            lds_dma16_at<KOFS + 8 * 256>(gk, koff[2], lds_row0);
-            lds_dma16_at<VOFS + 8 * 256>(gv, voff[2], lds_row0);
-            lds_dma16_at<KOFS + 12 * 256>(gk, koff[3], lds_row0);
-            lds_dma16_at<VOFS + 12 * 256>(gv, voff[3], lds_row0);
+            lds_dma16_at<KOFS + 0 * RPI * RB>(gk, koff[0], lds_row0);
+            lds_dma16_at<VOFS + 0 * RPI * RB>(gv, voff[0], lds_row0);
+            lds_dma16_at<KOFS + 1 * RPI * RB>(gk, koff[1], lds_row0);
+            lds_dma16_at<VOFS + 1 * RPI * RB>(gv, voff[1], lds_row0);
+            if constexpr (NI == 4) {
+                lds_dma16_at<KOFS + 2 * RPI * RB>(gk, koff[2], lds_row0);
+                lds_dma16_at<VOFS + 2 * RPI * RB>(gv, voff[2], lds_row0);
+                lds_dma16_at<KOFS + 3 * RPI * RB>(gk, koff[3], lds_row0);
+                lds_dma16_at<VOFS + 3 * RPI * RB>(gv, voff[3], lds_row0);
+            }
         };
         using Stg0 = std::integral_constant<int, 0>;
         using Stg1 = std::integral_constant<int, 1>;
         // keys at or past kv_end came from a clamped (allocated) page: zero
         // their V rows so that weight 0 times whatever was there stays 0
+        // (their scores are masked)
         auto zero_tail = [&](int tile, uint8_t *sV) {
             if ((tile + 1) * TN > kv_end) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (tile * TN + wrow + 4 * i + lrow >= kv_end)
-                        *(u32x4 *)(sV + (wrow + 4 * i) * 256 + 16 * lane) = u32x4{0, 0, 0, 0};
+                for (int i = 0; i < NI; ++i)
+                    if (tile * TN + wrow + RPI * i + lrow >= kv_end)
+                        *(u32x4 *)(sV + (wrow + RPI * i) * RB + 16 * lane) = u32x4{0, 0, 0, 0};
             }
         };
         if (n_it > 0) {
@@ -839,112 +931,7 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, int bx, int spli
             if (k + 1 < n_it)
                 step(k + 1, sK1, sV1, Stg0{}, sV0);
         }
-    } else {
-        // fp8 caches: codes are loaded into registers two tiles ahead (two
-        // register sets, so two tiles of loads are in flight during each
-        // compute), widened to the q dtype and written into the LDS stage.
-        // Thread unit i covers keys 2p, 2p+1 of the tile, p = tid/16 + 16i,
-        // and the d chunk c = tid%16 (d 8c .. 8c+7); one load instruction of a
-        // wave covers an 8-key group (one page), whose id is a scalar load
-        // fetched one tile before the loads that use it.
-        constexpr int PPT = (TN / 2) * 16 / NT;
-        const int c = gtid & 15;
-        const int lanep = 2 * ((gtid >> 4) & 3);
-        const uint32_t lofs0 = (uint32_t)(lanep * a.kv_st_slot + 8 * c) * KVB;
-        const uint32_t lofs1 = lofs0 + (uint32_t)a.kv_st_slot * KVB;
-        struct Codes {
-            u32x2 k[PPT][2], v[PPT][2];
-        };
-        int32_t blk_next[PPT];
-        Codes R0, R1;
-        auto fetch_ids = [&](int tile) {
-#pragma unroll
-            for (int i = 0; i < PPT; ++i) {
-                const int jb = tile * TN + 8 * wv + i * (NT / 8);
-                blk_next[i] = sload(btrow + min(jb >> lbs, last_page));
-            }
-        };
-        auto load_tile = [&](int tile, Codes &r) {
-#pragma unroll
-            for (int i = 0; i < PPT; ++i) {
-                const int jb = tile * TN + 8 * wv + i * (NT / 8);
-                const int64_t pofs =
-                    ((int64_t)blk_next[i] * a.kv_st_blk + (int64_t)(jb & bs_mask) * a.kv_st_slot) * KVB;
-                const uint8_t *pk = kbase + pofs;
-                const uint8_t *pv = vbase + pofs;
-                r.k[i][0] = *(const u32x2 *)(pk + lofs0);
-                r.k[i][1] = *(const u32x2 *)(pk + lofs1);
-                r.v[i][0] = *(const u32x2 *)(pv + lofs0);
-                r.v[i][1] = *(const u32x2 *)(pv + lofs1);
-            }
-        };
-        // Keys at or past kv_end were read from a clamped (allocated) page
-        // and must contribute nothing: their K and V rows are stored as 0.
-        // (Applied here, when the loaded registers are consumed anyway, and
-        // not at load time, which would make every load wait at once.)
-        auto store_tile = [&](int tile, const Codes &r, uint8_t *sK, uint8_t *sV) {
-            const bool full = (tile + 1) * TN <= kv_end;
-#pragma unroll
-            for (int i = 0; i < PPT; ++i) {
-                const int p = (gtid >> 4) + i * (NT / 16);
-                const int j0 = 2 * p, j1 = 2 * p + 1;
-                u32x4 k0 = widen_fp8<F16>(r.k[i][0]), k1 = widen_fp8<F16>(r.k[i][1]);
-                u32x4 v0 = widen_fp8<F16>(r.v[i][0]), v1 = widen_fp8<F16>(r.v[i][1]);
-                if (!full) {
-                    if (tile * TN + j0 >= kv_end) { k0 = u32x4{0, 0, 0, 0}; v0 = u32x4{0, 0, 0, 0}; }
-                    if (tile * TN + j1 >= kv_end) { k1 = u32x4{0, 0, 0, 0}; v1 = u32x4{0, 0, 0, 0}; }
-                }
-                *(u32x4 *)(sK + j0 * 256 + ((c ^ swz_k(j0)) << 4)) = k0;
-                *(u32x4 *)(sK + j1 * 256 + ((c ^ swz_k(j1)) << 4)) = k1;
-                *(u32x4 *)(sV + j0 * 256 + ((c ^ swz_v(j0)) << 4)) = v0;
-                *(u32x4 *)(sV + j1 * 256 + ((c ^ swz_v(j1)) << 4)) = v1;
-            }
-        };
-        // the group's k-th tile lives in register set R(k % 2) between its
-        // load and its store
-        if (n_it > 0) {
-            if (has(0)) {
-                fetch_ids(mine(0));
-                load_tile(mine(0), R0);
-            }
-            if (has(1)) {
-                fetch_ids(mine(1));
-                load_tile(mine(1), R1);
-            }
-            if (has(2))
-                fetch_ids(mine(2));
-            if (has(0))
-                store_tile(mine(0), R0, sK0, sV0);
-            __syncthreads();
-            if (has(2)) {
-                load_tile(mine(2), R0);
-                if (has(3))
-                    fetch_ids(mine(3));
-            }
-        }
-        // compute(k) reads one stage while the other receives tile k + 1
-        // (from set rn, which then receives tile k + 3)
-        auto step = [&](int k, uint8_t *cK, uint8_t *cV, uint8_t *nK, uint8_t *nV, Codes &rn) {
-            if (wave_on && has(k))
-                compute(mine(k), cK, cV);
-            if (k + 1 < n_it) {
-                if (has(k + 1))
-                    store_tile(mine(k + 1), rn, nK, nV);
-                loop_sync();
-                if (has(k + 3)) {
-                    load_tile(mine(k + 3), rn);
-                    if (has(k + 4))
-                        fetch_ids(mine(k + 4));
-                }
-            }
-        };
-        for (int k = 0; k < n_it; k += 2) {
-            step(k, sK0, sV0, sK1, sV1, R1);
-            if (k + 1 < n_it)
-                step(k + 1, sK1, sV1, sK0, sV0, R0);
-        }
     }
-
     // ---------------------------------------------------------------- epilogue
     if constexpr (KG == 1) {
         if (!wave_on)
