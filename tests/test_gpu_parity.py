@@ -551,6 +551,63 @@ def test_poisoned_unused_table_entries():
     assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
 
 
+def _poison_unused_slots(wl):
+    """A copy of wl whose cache slots outside every sequence's key range (the
+    tail of each last page, pages past it, pages no table names) hold NaN
+    (16-bit) or the e4m3fn NaN code 0x7f."""
+    NB, bs = wl.k_cache.shape[:2]
+    used = torch.zeros((NB, bs), dtype=torch.bool)
+    for s, kv in enumerate(wl.seqused_k.tolist()):
+        j = torch.arange(kv)
+        used[wl.block_table[s, j // bs].long(), j % bs] = True
+    assert (~used).any()
+    caches = []
+    for c in (wl.k_cache, wl.v_cache):
+        c = c.clone()
+        if c.dtype == torch.float8_e4m3fn:
+            c.view(torch.uint8)[~used] = 0x7F
+        else:
+            c.view(torch.int16)[~used] = 0x7FC0 if c.dtype == torch.bfloat16 else 0x7E00
+        assert torch.isnan(c[~used].float()).all()
+        caches.append(c)
+    return wk.Workload(**{**wl.__dict__, "k_cache": caches[0], "v_cache": caches[1]})
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+@pytest.mark.parametrize("bs", [16, 64])
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3fn"])
+def test_nan_in_unused_cache_slots(kv_dtype, bs, splits):
+    """Keys past a sequence's end are read from its last (or a clamped) page
+    whole tiles at a time; their scores are masked and their value rows zeroed,
+    so NaN there must not reach any output (decode and prefill rows, ragged
+    tails, full and split launches)."""
+    q_lens, kv_lens = [1, 40, 3, 130, 2], [77, 100, 3, 1037, 190]
+    wl = wk.make_paged("nanslots", 4390 + bs + splits + (kv_dtype != "bf16"), q_lens, kv_lens, 8, 2,
+                       block_size=bs, kv_dtype=kv_dtype, causal=True)
+    bad = _poison_unused_slots(wl)
+    H.say(f"NaN in unused cache slots {kv_dtype} bs {bs} splits {splits}")
+    out, lse = H.run(bad, num_splits=splits)
+    H.compare(wl, out, lse, what=f"nan slots {kv_dtype} bs {bs} splits {splits}")
+    ref, ref_lse = H.run(wl, num_splits=splits)
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16)) and torch.equal(lse, ref_lse)
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+def test_nan_in_unused_cache_slots_fp8_compute(splits):
+    """The same poisoning under the fp8-compute mode: the output equals that of
+    the clean cache bit for bit."""
+    wl = wk.make_paged("nanslots_f8c", 4480 + splits, [1, 40, 3, 130, 2], [77, 100, 3, 1037, 190], 8, 2,
+                       block_size=16, kv_dtype="fp8_e4m3fn", causal=True)
+    bad = _poison_unused_slots(wl)
+    H.say(f"NaN in unused cache slots, fp8 compute, splits {splits}")
+    out, lse = H.run(bad, num_splits=splits, fp8_compute=True)
+    ref, ref_lse = H.run(wl, num_splits=splits, fp8_compute=True)
+    plain, _ = H.run(wl, num_splits=splits)
+    assert not torch.equal(ref.view(torch.int16), plain.view(torch.int16))   # the mode did run
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16)) and torch.equal(lse, ref_lse)
+
+
 def test_deterministic():
     wl = wk.make_paged("det", 4400, [1, 64, 200], [1000, 300, 200], 8, 2, block_size=32, causal=True)
     H.say("determinism")
