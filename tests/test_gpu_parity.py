@@ -139,6 +139,13 @@ def test_config4_mixed_chunked_prefill():
     rows = H.sample_rows(wl, 500, seed=4)
     rows = rows[rows[:, 0] >= 64]
     H.compare(wl, out, lse, rows=rows, what="config4 prefill rows")
+    # every row of two whole (chunk, head) planes: the chunk with the longest
+    # cached prefix on the first head, the one with the shortest on the last
+    cu, kv = wl.cu_seqlens_q.numpy(), wl.seqused_k.numpy()
+    pre = [s for s in range(len(cu) - 1) if cu[s + 1] - cu[s] > 1]
+    planes = [(max(pre, key=lambda s: kv[s]), 0), (min(pre, key=lambda s: kv[s]), wl.num_q_heads - 1)]
+    rows = np.array([(t, h) for s, h in planes for t in range(cu[s], cu[s + 1])])
+    H.compare(wl, out, lse, rows=rows, what="config4 two whole prefill planes")
 
 
 def test_config5_long_context_fp8_32_splits():
