@@ -140,8 +140,9 @@ def test_backward_full_size_sampled():
     """The backward benchmark's shape (batch 4, 32 heads, N 4096, fp16, scale 1.3,
     causal), O and LSE from the HIP forward.  The oracle checks dQ of sampled
     rows (each as a one-row problem over the keys it sees) and dK, dV of the
-    last 48 keys of every sequence (only the last 48 rows see them), and the
-    dV rows of every (sequence, head) must sum to its dO rows."""
+    last 48 keys of every sequence (only the last 48 rows see them), every
+    entry of two whole (sequence, head) planes, and the dV rows of every
+    (sequence, head) must sum to its dO rows."""
     case = wk.backward_bench()
     causal = True
     N, H = 4096, 32
@@ -179,6 +180,17 @@ def test_backward_full_size_sampled():
         want = dO.sum(axis=0)
         tol = 2 * u * np.abs(dO).sum(axis=0) + 1e-3
         assert (np.abs(sum_dv - want) <= tol).all(), f"seq {s}: dV rows do not sum to the dO rows"
+    # every dQ, dK and dV entry of two whole (sequence, head) planes
+    for s, h in ((0, 0), (3, H - 1)):
+        base = s * N
+        sub = {"q": case["q"][base:base + N, h:h + 1], "k": case["k"][base:base + N, h:h + 1],
+               "v": case["v"][base:base + N, h:h + 1], "dout": case["dout"][base:base + N, h:h + 1],
+               "cu_seqlens_q": torch.tensor([0, N], dtype=torch.int32),
+               "cu_seqlens_k": torch.tensor([0, N], dtype=torch.int32),
+               "softmax_scale": case["softmax_scale"]}
+        ref = oracle_case(sub, causal)
+        plane = {n: got[n][base:base + N, h:h + 1] for n in ("dq", "dk", "dv")}
+        check_close(plane, ref, u, f"whole plane (sequence {s}, head {h})", "backward full size")
     assert np.isfinite(got["dq"]).all() and np.isfinite(got["dk"]).all() and np.isfinite(got["dv"]).all()
 
 
