@@ -1426,21 +1426,23 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, int bx, int split
         ids[1] = sload(btrow + min((u * UK + 16) >> lbs, last_page));
     };
 
-    // K and V: 16-bit caches, instruction i covers keys 4i .. 4i+3 of the
-    // unit (16 lanes x 16 bytes per key row); fp8 caches, keys 8i .. 8i+7 (8
-    // lanes x 16 bytes = 16 codes each).  One page per instruction, whole rows
-    // per instruction (coalesced).  Both go through the wave's own LDS stages
-    // (K with the swz_k layout the score fragments are read from, V with swz_v).
-    constexpr int VKI = FP8KV ? 8 : 4;          // keys per instruction
+    // K and V: instruction i covers keys 4i .. 4i+3 of the unit, 16 lanes
+    // per key row (16 bytes of a 16-bit row, 8 codes of an fp8 row).  One
+    // page per instruction, whole rows per instruction (coalesced).  Both go
+    // through the wave's own LDS stages (K with the swz_k layout the score
+    // fragments are read from, V with swz_v), lane l writing granule l % 16
+    // of its row (an fp8 lane's 8 codes widen to one granule), so each
+    // 16-lane store pass covers the 16 positions of one row.
+    constexpr int VKI = 4;                      // keys per instruction
     constexpr int VNI = UK / VKI;               // instructions per unit
-    constexpr int VLK = 64 / VKI;               // lanes per key
-    const int vkey = lane / VLK;
-    const int vch = lane % VLK;                 // 16-byte chunk of the cached row
-    const uint32_t vlofs = (uint32_t)(vkey * a.kv_st_slot * KVB + 16 * vch);
+    const int vkey = lane >> 4;
+    const int vch = lane & 15;                  // granule of the row (16-bit)
+    const uint32_t vlofs = (uint32_t)(vkey * a.kv_st_slot * KVB + 16 * KVB / 2 * vch);
     // units in flight per wave: two for fp8 caches (their register sets are
     // half as large), one for 16-bit caches (a second set would spill)
     constexpr int NSET = FP8KV ? 2 : 1;
-    u32x4 kr[NSET][VNI], vr[NSET][VNI];
+    using LT = std::conditional_t<FP8KV, u32x2, u32x4>;   // one lane's share of a row
+    LT kr[NSET][VNI], vr[NSET][VNI];
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, NSET - 1>;
     auto load_kv = [&](int u, auto set) {
@@ -1452,8 +1454,8 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, int bx, int split
                                   (int64_t)(jb & bs_mask) * a.kv_st_slot) * KVB;
             // streamed once: non-temporal, so the stream does not evict
             // what other workgroups reuse from the L2
-            kr[SI][i] = __builtin_nontemporal_load((const u32x4 *)(kbase + pofs + vlofs));
-            vr[SI][i] = __builtin_nontemporal_load((const u32x4 *)(vbase + pofs + vlofs));
+            kr[SI][i] = __builtin_nontemporal_load((const LT *)(kbase + pofs + vlofs));
+            vr[SI][i] = __builtin_nontemporal_load((const LT *)(vbase + pofs + vlofs));
         }
     };
     uint8_t *const sK = lds + wv * (2 * VST);
@@ -1464,20 +1466,18 @@ __device__ __forceinline__ void decode_body(const AttnArgs &a, int bx, int split
 #pragma unroll
         for (int i = 0; i < VNI; ++i) {
             const int row = VKI * i + vkey;
-            u32x4 v = vr[SI][i];
+            u32x4 k, v;
+            if constexpr (FP8KV) {
+                k = widen_fp8<F16>(kr[SI][i]);  // 8 codes = d 8vch .. 8vch+7 = granule vch
+                v = widen_fp8<F16>(vr[SI][i]);
+            } else {
+                k = kr[SI][i];
+                v = vr[SI][i];
+            }
             if (!full && u * UK + row >= kv_end)
                 v = u32x4{0, 0, 0, 0};          // clamped-page keys weigh 0; zero their values
-            if constexpr (FP8KV) {
-                // 16 codes = d 16vch .. 16vch+15 -> granules 2vch, 2vch+1
-                const int g0 = 2 * vch;
-                *(u32x4 *)(sK + row * 256 + ((g0 ^ swz_k(row)) << 4)) = widen_fp8<F16>(u32x2{kr[SI][i][0], kr[SI][i][1]});
-                *(u32x4 *)(sK + row * 256 + (((g0 + 1) ^ swz_k(row)) << 4)) = widen_fp8<F16>(u32x2{kr[SI][i][2], kr[SI][i][3]});
-                *(u32x4 *)(sV + row * 256 + ((g0 ^ swz_v(row)) << 4)) = widen_fp8<F16>(u32x2{v[0], v[1]});
-                *(u32x4 *)(sV + row * 256 + (((g0 + 1) ^ swz_v(row)) << 4)) = widen_fp8<F16>(u32x2{v[2], v[3]});
-            } else {
-                *(u32x4 *)(sK + row * 256 + ((vch ^ swz_k(row)) << 4)) = kr[SI][i];
-                *(u32x4 *)(sV + row * 256 + ((vch ^ swz_v(row)) << 4)) = v;
-            }
+            *(u32x4 *)(sK + row * 256 + ((vch ^ swz_k(row)) << 4)) = k;
+            *(u32x4 *)(sV + row * 256 + ((vch ^ swz_v(row)) << 4)) = v;
         }
     };
 
