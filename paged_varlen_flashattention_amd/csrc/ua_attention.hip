@@ -994,14 +994,16 @@ __device__ __forceinline__ void prefill_body(const AttnArgs &a, int bx, int spli
 //
 // LDS layouts of a 64-key tile (128-byte rows of codes, 16-byte chunks):
 //   K: chunk c of key k at c ^ gk(k), gk = ((k >> 1) & 3) | (((k >> 4) & 1) << 2);
-//   V: chunk c of key k at c ^ ((k >> 1) & 3).
+//   V: chunk c of key k at c ^ 2((k >> 1) & 3), so the 32 lanes of an 8-bit
+//      transposing read (8 consecutive keys x chunks 2x, 2x+1) hit 32
+//      distinct 8-byte bank groups.
 // MFMA row i of a 32-key score block reads key pk(i) = 16((i >> 2) & 1) +
 // 4(i >> 3) + (i & 3), which puts keys 16h .. 16h+15 of the block in
 // accumulator registers 0..15 of lane half h: the 32 weights a lane holds are
 // the bytes of its P^T operand, and the V^T operand gathers the same keys with
 // four 8-bit transposing reads.
 __device__ __forceinline__ int gk_swz(int k) { return ((k >> 1) & 3) | (((k >> 4) & 1) << 2); }
-__device__ __forceinline__ int gv_swz(int k) { return (k >> 1) & 3; }
+__device__ __forceinline__ int gv_swz(int k) { return 2 * ((k >> 1) & 3); }
 __device__ __forceinline__ int pk_row(int i) { return 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3); }
 
 template <bool F16, bool CAUSAL, bool SPLIT, int KG>
